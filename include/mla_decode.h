@@ -1,0 +1,201 @@
+/*
+ * mla_decode.h - C ABI of the MLA decode library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is DeepSeek-R1 forward_absorb Multi-head Latent Attention
+ * decode as the kernelbot-amd-mixed-mla submission template (submission 675627)
+ * defines it in its docstring ("DeepSeek R1 forward_absorb MLA config", "KV
+ * buffer format", "Input tuple", "Output"): 16 query heads share one latent KV
+ * head; for sequence b, query row t and head h
+ *
+ *     s_j      = sm_scale * sum_{d<576} q[t,h,d] * kv[j,d]
+ *     out[t,h,v] = sum_j softmax_j(s) * kv[j,v]          (v < 512)
+ *
+ * over the KV rows j in [kv_indptr[b], kv_indptr[b+1]).  Keys are the full
+ * 576-wide row (512 latent + 64 rope), values the first 512 columns of the same
+ * row.  The work is split along the KV rows ("split-K" flash decoding, the
+ * two-stage scheme of submissions 586148 and 753817): stage 1 turns each
+ * workgroup's slice into a partial output plus its log-sum-exp, stage 2 merges
+ * the slices of a sequence with LSE weights.
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are HIP device addresses; host pointers are plain host
+ *     memory.  Every device buffer is owned by the caller and must stay valid
+ *     until the work queued on `stream` has finished.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the null stream).
+ *   - Entry points return a status and never throw.  MLA_ERR_HIP keeps the last
+ *     HIP error, which mla_last_error_string() describes.
+ *   - Thread safety: plans are immutable after creation and may be shared;
+ *     runs on different streams need separate workspaces.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size, workspace too small, bad indptr */
+  MLA_ERR_UNSUPPORTED = 2, /* shape or dtype combination this build does not implement */
+  MLA_ERR_HIP = 3          /* a HIP call or kernel launch failed */
+} mla_status;
+
+typedef enum mla_dtype {
+  MLA_DTYPE_BF16 = 0,       /* bfloat16, 2 bytes per element */
+  MLA_DTYPE_FP8_E4M3FN = 1, /* OCP fp8 E4M3FN code, 1 byte, with one fp32 scale per tensor */
+  MLA_DTYPE_MXFP4 = 2       /* OCP MXFP4: E2M1 pairs (element 2i in the low nibble) + one
+                               E8M0 scale byte per 32 elements; KV only */
+} mla_dtype;
+
+/* The decode problem a plan is made for. */
+typedef struct mla_problem {
+  int32_t batch_size; /* sequences; >= 1 */
+  int32_t total_q;    /* rows of q and out; must equal batch_size (one query token per sequence) */
+  int64_t total_kv;   /* rows in the KV buffer; kv_indptr[batch_size] <= total_kv < 2^31 */
+  int32_t num_heads;  /* query heads; must be 16 */
+  int32_t qk_dim;     /* key width; must be 576 (512 latent + 64 rope) */
+  int32_t v_dim;      /* value width; must be 512 (first columns of the KV row) */
+  int32_t q_dtype;    /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3FN */
+  int32_t kv_dtype;   /* any mla_dtype; fp8 q requires fp8 KV */
+  float sm_scale;     /* softmax scale, 1/sqrt(576) for DeepSeek-R1 */
+  int32_t num_cus;    /* compute units to plan for; 0 = ask the current HIP device */
+} mla_problem;
+
+/* Optional planner overrides (NULL = planner's choice for every field). */
+typedef struct mla_plan_options {
+  int32_t rows_per_split; /* > 0: KV rows each stage-1 workgroup takes (rounded up to 32) */
+  int32_t wgs_per_cu;     /* > 0: resident stage-1 workgroups per CU the planner targets */
+} mla_plan_options;
+
+/* What a plan decided (for tests, benchmarks and logs). */
+typedef struct mla_plan_desc {
+  int32_t num_splits;      /* stage-1 workgroups G; workgroup g owns KV rows [g*R, min((g+1)*R, total_kv)) */
+  int32_t rows_per_split;  /* R, a multiple of tile_rows */
+  int32_t tile_rows;       /* KV rows per LDS tile */
+  int32_t stages;          /* depth of the LDS tile ring */
+  int32_t partial_slots;   /* 2*G partial (O, LSE) slots in the workspace */
+  int32_t stage2;          /* 1 if mla_decode_run launches the LSE-merge kernel */
+  int64_t workspace_bytes; /* bytes mla_decode_run needs */
+  int32_t lds_bytes;       /* LDS per stage-1 workgroup */
+  int32_t num_cus;         /* compute units planned for */
+} mla_plan_desc;
+
+typedef struct mla_plan mla_plan;
+
+/*
+ * Plan a decode.  Host-only: no device memory is touched and no HIP call is
+ * made unless problem->num_cus == 0.
+ *   problem         shape and dtypes (see mla_problem).
+ *   options         NULL or overrides.
+ *   kv_indptr_host  NULL, or the host copy of kv_indptr (batch_size + 1 int32,
+ *                   non-decreasing, kv_indptr[0] >= 0, last <= total_kv).  With it the
+ *                   planner checks the offsets and skips stage 2 when every
+ *                   sequence is non-empty and lies inside one workgroup's rows;
+ *                   the plan is then valid only for runs with those offsets.
+ *                   Without it the plan is valid for any offsets with the same
+ *                   batch_size and total_kv.
+ *   plan_out        receives a library-owned plan; free with mla_decode_plan_destroy.
+ *   workspace_bytes receives the size of the device workspace run needs.
+ * Returns MLA_ERR_UNSUPPORTED for shapes/dtypes outside this build and
+ * MLA_ERR_INVALID_ARG for bad arguments; *plan_out is NULL on failure.
+ */
+mla_status mla_decode_plan(const mla_problem* problem, const mla_plan_options* options,
+                           const int32_t* kv_indptr_host, mla_plan** plan_out, size_t* workspace_bytes);
+
+/*
+ * Run a planned decode asynchronously on `stream` (stage 1, then stage 2 when
+ * the plan needs it).  No allocation, no host<->device copy, no synchronisation.
+ * All device pointers must be 16-byte aligned.
+ *   q          device, [total_q][16][576]: bf16, or fp8 E4M3FN codes when q_dtype is fp8.
+ *   q_scale    device fp32[1] (fp8 q: q = code * q_scale); ignored for bf16 q (may be NULL).
+ *   kv         device, [total_kv][576] bf16 | [total_kv][576] fp8 codes | [total_kv][288] MXFP4 bytes.
+ *   kv_scale   fp8 KV: device fp32[1] (kv = code * kv_scale).
+ *              MXFP4 KV: device uint8 [total_kv][18] E8M0 bytes, one per 32 columns,
+ *              read in 16-byte units: the allocation must be readable up to the next
+ *              multiple of 16 bytes past total_kv*18.
+ *              bf16 KV: ignored (may be NULL).
+ *   qo_indptr  device int32[batch_size + 1]; qo_indptr[b] is sequence b's query row.
+ *   kv_indptr  device int32[batch_size + 1]; sequence b owns KV rows
+ *              [kv_indptr[b], kv_indptr[b+1]).  Values inconsistent with the plan
+ *              (or decreasing) give undefined output, but every access stays inside
+ *              [0, total_kv) rows.
+ *   out        device bf16 [total_q][16][512]; a sequence with no KV rows gets zeros.
+ *   workspace  device scratch of at least the planned workspace_bytes (contents
+ *              need not be initialised; they are overwritten).
+ */
+mla_status mla_decode_run(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
+                          const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of mla_decode_run as separate calls, for callers that put
+ * work or an exchange between them (for example merging partials produced on
+ * several devices) and for per-stage timing.  mla_decode_split with the same
+ * arguments as mla_decode_run launches stage 1 only: each workgroup's online
+ * softmax over its KV rows, writing whole sequences to `out` and the
+ * partial (O, LSE) of split sequences to the workspace (the split-K stage 1 of
+ * submissions 586148 / 753817).  mla_decode_merge launches stage 2 only: for
+ * each sequence split across workgroups, out = sum_s w_s O_s / sum_s w_s with
+ * w_s = exp(LSE_s - max LSE), and zeros for sequences with no KV rows; it
+ * does nothing when the plan needs no stage 2.  Calling split then merge on
+ * one stream equals mla_decode_run.
+ */
+mla_status mla_decode_split(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
+                            const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+mla_status mla_decode_merge(const mla_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Free a plan (NULL is accepted). */
+void mla_decode_plan_destroy(mla_plan* plan);
+
+/* Copy what the plan decided into *desc. */
+mla_status mla_decode_plan_describe(const mla_plan* plan, mla_plan_desc* desc);
+
+/*
+ * Host replay of how stage 1 cuts the batch (the same piece rule the kernel
+ * uses), for tests and tooling.  Writes up to `capacity` records of 5 int64
+ * each: {workgroup g, sequence b, first row, end row, slot (-1 = written to out
+ * directly)} in workgroup order, and the total number of records to *count.
+ * kv_indptr_host as in mla_decode_plan (required here).
+ */
+mla_status mla_decode_plan_pieces(const mla_plan* plan, const int32_t* kv_indptr_host, int64_t* records,
+                                  int64_t capacity, int64_t* count);
+
+/*
+ * Partial slots stage 2 merges for sequence b (host replay of the stage-2
+ * rule).  Writes up to `capacity` slot indices to `slots` and the number of
+ * slots to *count (0 when the sequence was written directly or is empty).
+ */
+mla_status mla_decode_plan_merge_slots(const mla_plan* plan, const int32_t* kv_indptr_host, int32_t b,
+                                       int32_t* slots, int32_t capacity, int32_t* count);
+
+/*
+ * Decode stored KV codes to fp32 with the device functions the decode kernel
+ * uses (for bit-exactness tests of the dequantisation).
+ *   MLA_DTYPE_FP8_E4M3FN: codes = n bytes, scales = device fp32[1] or NULL (1.0);
+ *                         out[i] = fp32(value(code_i)) * scale, one fp32 rounding.
+ *   MLA_DTYPE_MXFP4:      codes = n rows of 288 bytes, scales = n rows of 18 bytes;
+ *                         out = n x 576 values, each the bf16 the kernel feeds to its
+ *                         matrix instructions, widened to fp32.
+ *   MLA_DTYPE_BF16:       codes = n bf16 values; out[i] = fp32(code_i).
+ * Device pointers, asynchronous on `stream`.
+ */
+mla_status mla_debug_decode(int32_t kv_dtype, const void* codes, const void* scales, float* out, int64_t n,
+                            void* stream);
+
+/* Human-readable status name. */
+const char* mla_status_string(mla_status status);
+
+/* Description of the last HIP error seen by this thread ("" if none). */
+const char* mla_last_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,192 @@
+"""C ABI and host planner (no GPU): the library loads and exports every entry
+point the header declares; the planner's cut of the batch covers every KV row
+exactly once and stage 2 merges exactly the pieces stage 1 leaves partial;
+argument errors return status codes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_decode_split_amd as mla
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("mla_decode_plan", "mla_decode_run", "mla_decode_plan_destroy", "mla_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function():
+    lib = mla.library()
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding exposes the same names
+    assert all(hasattr(mla, n) for n in _declared_functions() if n != "mla_last_error_string")
+
+
+def test_status_strings():
+    assert mla.mla_status_string(0) == "MLA_OK"
+    assert mla.mla_status_string(2) == "MLA_ERR_UNSUPPORTED"
+
+
+def _plan(bs, total_kv, kv="fp8", q="bf16", ind=None, rows=0, cus=256, **kw):
+    prob = mla.make_problem(bs, total_kv, q, kv, num_cus=cus, **kw)
+    opts = mla.mla_plan_options(rows, 0) if rows else None
+    return mla.mla_decode_plan(prob, opts, ind)
+
+
+def _indptr(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_plans_for_the_five_workloads(name):
+    lengths = synth.workload_lengths(name)
+    spec = synth.WORKLOADS[name]
+    ind = _indptr(lengths)
+    plan = _plan(len(lengths), int(ind[-1]), spec["kv_dtype"], spec["q_dtype"], ind)
+    d = mla.mla_decode_plan_describe(plan)
+    assert d["num_splits"] * d["rows_per_split"] >= ind[-1] > (d["num_splits"] - 1) * d["rows_per_split"]
+    assert d["rows_per_split"] % d["tile_rows"] == 0
+    assert d["partial_slots"] == 2 * d["num_splits"]
+    assert d["lds_bytes"] * 2 <= 160 * 1024
+    assert plan.workspace_bytes >= d["partial_slots"] * 16 * 513 * 4
+    _check_cut(plan, ind)
+
+
+def _check_cut(plan, ind):
+    d = mla.mla_decode_plan_describe(plan)
+    rec = mla.mla_decode_plan_pieces(plan, ind)
+    bs = len(ind) - 1
+    R, G = d["rows_per_split"], d["num_splits"]
+    covered = np.zeros(int(ind[-1]), dtype=np.int32)
+    slots_of = {b: [] for b in range(bs)}
+    used = set()
+    for g, b, r0, r1, slot in rec:
+        assert ind[b] <= r0 < r1 <= ind[b + 1]
+        assert g * R <= r0 and r1 <= min((g + 1) * R, ind[-1])
+        covered[r0:r1] += 1
+        if slot >= 0:
+            assert slot < d["partial_slots"] and slot // 2 == g
+            assert slot not in used
+            used.add(int(slot))
+            slots_of[b].append(int(slot))
+        else:
+            assert r0 == ind[b] and r1 == ind[b + 1]  # direct pieces are whole sequences
+    assert np.all(covered == 1), "every KV row of every sequence exactly once"
+    needs_merge = False
+    for b in range(bs):
+        merge = mla.mla_decode_plan_merge_slots(plan, ind, b)
+        assert sorted(merge) == sorted(slots_of[b])
+        assert len(merge) != 1
+        needs_merge |= len(merge) > 0 or ind[b + 1] == ind[b]
+    if not needs_merge:
+        assert d["stage2"] == 0
+    else:
+        assert d["stage2"] == 1
+
+
+@pytest.mark.parametrize("lengths,rows", [
+    ([1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129], 32),
+    ([1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129], 96),
+    ([0, 5, 0, 0, 300, 0], 64),
+    ([4096] * 3, 1024),
+    ([1] * 200, 32),
+    ([700, 1000, 33], 0),
+])
+def test_cut_properties(lengths, rows):
+    ind = _indptr(lengths)
+    plan = _plan(len(lengths), int(ind[-1]), ind=ind, rows=rows)
+    _check_cut(plan, ind)
+
+
+def test_random_ragged_cuts(rng):
+    for trial in range(30):
+        bs = int(rng.integers(1, 60))
+        lengths = rng.integers(0, 3000, size=bs)
+        lengths[rng.random(bs) < 0.1] = 0
+        ind = _indptr(lengths)
+        if ind[-1] == 0:
+            continue
+        rows = int(rng.choice([0, 32, 64, 96, 512, 2048]))
+        plan = _plan(bs, int(ind[-1]) + int(rng.integers(0, 50)), ind=ind, rows=rows, cus=int(rng.choice([8, 256])))
+        _check_cut(plan, ind)
+
+
+def test_uniform_batch_without_host_indptr_keeps_stage2():
+    plan = _plan(4, 4096)
+    assert mla.mla_decode_plan_describe(plan)["stage2"] == 1
+
+
+def test_single_split_batch_skips_stage2():
+    ind = _indptr([100, 100, 100, 100])
+    plan = _plan(4, 400, ind=ind, rows=128)
+    d = mla.mla_decode_plan_describe(plan)
+    # sequence 1 spans rows 100..200 across the 128-row boundary -> merge needed
+    assert d["stage2"] == 1
+    ind2 = _indptr([64, 64, 64, 64])
+    d2 = mla.mla_decode_plan_describe(_plan(4, 256, ind=ind2, rows=128))
+    assert d2["stage2"] == 0
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except mla.MlaError as e:
+        return e.status
+    return mla.MLA_OK
+
+
+def test_plan_argument_errors():
+    unsupported = [
+        dict(num_heads=8), dict(qk_dim=512), dict(v_dim=576), dict(total_q=8),
+    ]
+    for kw in unsupported:
+        prob = mla.make_problem(4, 100, num_cus=256, **kw)
+        assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_UNSUPPORTED, kw
+    prob = mla.make_problem(4, 100, q_dtype="mxfp4", num_cus=256)
+    assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_UNSUPPORTED
+    prob = mla.make_problem(0, 100, num_cus=256)
+    assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG
+    prob = mla.make_problem(3, 100, num_cus=256)
+    assert _status(mla.mla_decode_plan, prob, None, np.array([0, 50, 40, 100], np.int32)) == mla.MLA_ERR_INVALID_ARG
+    assert _status(mla.mla_decode_plan, prob, None, np.array([0, 50, 60, 101], np.int32)) == mla.MLA_ERR_INVALID_ARG
+    assert mla.library().mla_decode_plan(None, None, None, None, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_run_argument_errors_before_any_launch():
+    """Validation happens on the host before anything touches a device, so fake
+    (never dereferenced) addresses are enough here."""
+    plan = _plan(2, 64, kv="fp8", ind=_indptr([32, 32]))
+    A = 1 << 20  # 16-byte aligned fake address
+    ok = dict(q=A, q_scale=A, kv=A, kv_scale=A, qo=A, kvp=A, out=A, ws=A, n=plan.workspace_bytes)
+
+    def run(**kw):
+        a = dict(ok, **kw)
+        return _status(mla.mla_decode_run, plan, a["q"], a["q_scale"], a["kv"], a["kv_scale"], a["qo"], a["kvp"],
+                       a["out"], a["ws"], a["n"])
+
+    assert run(q=None) == mla.MLA_ERR_INVALID_ARG
+    assert run(kv_scale=None) == mla.MLA_ERR_INVALID_ARG      # fp8 KV needs its scale
+    assert run(out=A + 2) == mla.MLA_ERR_INVALID_ARG          # misaligned
+    assert run(n=plan.workspace_bytes - 1) == mla.MLA_ERR_INVALID_ARG
+    assert run(ws=None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.library().mla_decode_run(None, A, A, A, A, A, A, A, A, 1 << 30, None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.library().mla_debug_decode(7, A, A, A, 10, None) == mla.MLA_ERR_UNSUPPORTED
+    assert mla.library().mla_debug_decode(2, A, None, A, 10, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_plan_destroy_accepts_null():
+    mla.library().mla_decode_plan_destroy(None)

@@ -1,0 +1,237 @@
+"""GPU parity of the HIP decode against the CPU fp64 oracle (MI355X only).
+
+Every call goes through the C ABI (mla_decode_plan / mla_decode_run /
+mla_debug_decode) via the ctypes binding.  Tolerances (bf16 output against the
+fp64 oracle): max |gpu - oracle| <= 2e-2 and ||gpu - oracle||_2 / ||oracle||_2
+<= 1e-2 over the compared outputs; the dequantisation check is bit-exact.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import mla_decode_split_amd as mla
+from mla_decode_split_amd import device as dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-2
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def _bf16_out_to_f64(out: torch.Tensor) -> np.ndarray:
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def _compare(got, ref, what):
+    diff = np.abs(got - ref)
+    max_abs = float(diff.max()) if diff.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    _say(f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert max_abs <= MAX_ABS, f"{what}: max_abs {max_abs}"
+    assert rel <= REL_L2, f"{what}: rel_l2 {rel}"
+    return max_abs, rel
+
+
+def _check_batch(w, rows_per_split=0, seq_ids=None, use_host_indptr=True, poison=True, what=""):
+    _say(f"case {what or w.name}: bs={w.batch_size} total_kv={w.total_kv} q={w.q_dtype} kv={w.kv_dtype} "
+         f"rows_per_split={rows_per_split}")
+    b = dev.upload(w)
+    plan = dev.plan_for(b, rows_per_split=rows_per_split, use_host_indptr=use_host_indptr)
+    ws = dev.workspace_for(plan, fill=float("nan") if poison else None)
+    out = torch.full((b.total_q, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dev.run(plan, b, out, ws)
+    torch.cuda.synchronize()
+    got = _bf16_out_to_f64(out)
+    ref, _ = oracle.decode_workload(w, seq_ids=seq_ids, threads=8)
+    if seq_ids is not None:
+        got, ref = got[seq_ids], ref[seq_ids]
+    return _compare(got, ref, what or w.name), plan, out
+
+
+# ------------------------------------------------------------- dequantisation
+
+def test_fp8_decode_bit_exact():
+    codes = np.arange(256, dtype=np.uint8)
+    for scale in (1.0, 0.37, 2.0 ** -7):
+        d_codes = torch.from_numpy(codes).cuda()
+        d_scale = torch.tensor([scale], dtype=torch.float32, device="cuda")
+        out = torch.empty(256, dtype=torch.float32, device="cuda")
+        mla.mla_debug_decode("fp8", d_codes, d_scale, out, 256)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ref = (oracle.decode_fp8(codes, float(np.float32(scale)))).astype(np.float32)  # one rounding to fp32
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32)), f"scale {scale}"
+
+
+def test_mxfp4_decode_bit_exact():
+    # every byte value (both nibble positions) under every scale code 2..252,
+    # where e2m1 * 2^(e-127) is a normal bf16/fp32 number
+    rows = 251
+    byte_vals = np.arange(256, dtype=np.uint8)
+    packed = np.tile(np.concatenate([byte_vals, byte_vals[:32]]), (rows, 1))
+    scales = np.repeat(np.arange(2, 253, dtype=np.uint8)[:, None], 18, axis=1)
+    scales[::3, 5] = 127
+    d_p = torch.from_numpy(packed).cuda()
+    d_s = torch.from_numpy(np.concatenate([scales.reshape(-1), np.zeros(16, np.uint8)])).cuda()
+    out = torch.empty((rows, 576), dtype=torch.float32, device="cuda")
+    mla.mla_debug_decode("mxfp4", d_p, d_s, out, rows)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.decode_mxfp4(packed, scales).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_mxfp4_decode_extreme_scales_report():
+    """Scale codes whose products leave the normal range: report what the
+    hardware gives (recorded in the design notes); finite normal results must
+    still be exact."""
+    codes = np.array([0, 1, 253, 254], dtype=np.uint8)
+    packed = np.tile(np.concatenate([np.arange(256, dtype=np.uint8), np.arange(32, dtype=np.uint8)]), (4, 1))
+    scales = np.repeat(codes[:, None], 18, axis=1)
+    d_p = torch.from_numpy(packed).cuda()
+    d_s = torch.from_numpy(np.concatenate([scales.reshape(-1), np.zeros(16, np.uint8)])).cuda()
+    out = torch.empty((4, 576), dtype=torch.float32, device="cuda")
+    mla.mla_debug_decode("mxfp4", d_p, d_s, out, 4)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.decode_mxfp4(packed, scales)
+    for r, c in enumerate(codes):
+        exact = got[r] == ref[r]
+        _say(f"e8m0={c}: {int(exact.sum())}/576 exact; sample got={got[r][:4]} ref={ref[r][:4]}")
+        normal = (np.abs(ref[r]) >= 2.0 ** -126) & (np.abs(ref[r]) < 3.3e38)
+        assert np.all(exact[normal])
+
+
+def test_bf16_decode_passthrough():
+    x = synth.normal_bf16(11, 1, 1000)
+    out = torch.empty(1000, dtype=torch.float32, device="cuda")
+    mla.mla_debug_decode("bf16", torch.from_numpy(x.view(np.int16)).cuda(), None, out, 1000)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), synth.bf16_to_f32(x))
+
+
+# ------------------------------------------------------------- small batches, full comparison
+
+EDGE_LENGTHS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257]
+COMBOS = [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8"), ("bf16", "mxfp4"), ("fp8", "bf16"), ("fp8", "mxfp4")]
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", COMBOS)
+def test_edge_lengths_all_formats(q_dtype, kv_dtype):
+    w = synth.make_batch(EDGE_LENGTHS, q_dtype, kv_dtype, seed=101, name=f"edges-{q_dtype}-{kv_dtype}")
+    _check_batch(w, what=f"edge lengths {q_dtype}/{kv_dtype}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("rows", [32, 96, 224, 512, 2048])
+def test_forced_split_counts(kv_dtype, rows):
+    # lengths 700, 1000, 33 -> splits per sequence range from 1 to 32
+    w = synth.make_batch([700, 1000, 33], "bf16", kv_dtype, seed=202, name="forced")
+    _check_batch(w, rows_per_split=rows, what=f"forced rows_per_split={rows} kv={kv_dtype}")
+
+
+def test_empty_sequences_give_zero():
+    w = synth.make_batch([0, 40, 0, 300, 0], "bf16", "fp8", seed=303, name="empties")
+    (_, _), plan, out = _check_batch(w, rows_per_split=64, what="empty sequences")
+    o = out.float().cpu().numpy()
+    assert np.all(o[[0, 2, 4]] == 0.0)
+
+
+def test_plan_without_host_indptr_matches():
+    w = synth.make_batch([100, 7, 900, 64], "bf16", "fp8", seed=404, name="no-host-indptr")
+    _check_batch(w, use_host_indptr=False, rows_per_split=128, what="plan without host indptr")
+    _check_batch(w, use_host_indptr=True, rows_per_split=2048, what="single split per sequence (no stage 2)")
+
+
+def test_long_single_sequence():
+    w = synth.make_batch([20000], "bf16", "fp8", seed=505, name="long")
+    _check_batch(w, what="one sequence of 20000 rows")
+
+
+def test_unaligned_mxfp4_scale_rows():
+    # sequence starts at odd rows so tiles begin at scale offsets that are not 16-byte aligned
+    w = synth.make_batch([1, 3, 5, 77, 129, 1000], "bf16", "mxfp4", seed=606, name="mx-unaligned")
+    for rows in (32, 64, 160):
+        _check_batch(w, rows_per_split=rows, what=f"mxfp4 unaligned starts rows={rows}")
+
+
+def test_runs_are_deterministic():
+    w = synth.make_batch([3000, 17, 4000], "bf16", "fp8", seed=707, name="det")
+    b = dev.upload(w)
+    plan = dev.plan_for(b)
+    o1 = dev.run(plan, b).clone()
+    o2 = dev.run(plan, b)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_run_on_a_side_stream():
+    w = synth.make_batch([500, 600], "bf16", "fp8", seed=808, name="stream")
+    b = dev.upload(w)
+    plan = dev.plan_for(b, rows_per_split=128)
+    s = torch.cuda.Stream()
+    out = torch.empty((2, 16, 512), dtype=torch.bfloat16, device="cuda")
+    ws = dev.workspace_for(plan)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        dev.run(plan, b, out, ws, stream=s)
+    s.synchronize()
+    ref, _ = oracle.decode_workload(w, threads=8)
+    _compare(_bf16_out_to_f64(out), ref, "side stream")
+
+
+# ------------------------------------------------------------- the five workloads
+
+SAMPLE = {
+    "bs4_kv1024_bf16": None,            # whole batch
+    "bs32_kv1024_fp8": None,            # whole batch
+    "bs64_kv8192_fp8": [0, 1, 17, 31, 32, 50, 63],
+    "bs256_kv8192_a8w8": [0, 1, 64, 127, 128, 200, 255],
+}
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_parity_at_full_size(name):
+    w = synth.make_workload(name)
+    if name in SAMPLE:
+        ids = SAMPLE[name]
+    else:  # ragged: the shortest, the longest and a spread in between
+        lengths = np.diff(w.kv_indptr)
+        order = np.argsort(lengths)
+        ids = sorted(set(order[[0, 1, 2, len(order) // 2, -3, -2, -1]].tolist()))
+    _check_batch(w, seq_ids=ids, poison=False, what=f"{name} (sequences {ids if ids else 'all'})")
+    # properties that hold for every output: finite, and each output column a
+    # convex combination of the value rows (|out| <= max |V| + bf16 rounding)
+    b = dev.upload(w)
+    plan = dev.plan_for(b)
+    out = dev.run(plan, b)
+    torch.cuda.synchronize()
+    o = out.float()
+    assert bool(torch.isfinite(o).all())
+    if w.kv_dtype == "bf16":
+        bound = float(np.abs(synth.bf16_to_f32(w.kv[:, :512])).max())
+    elif w.kv_dtype == "fp8":
+        bound = 448.0 * float(w.kv_scale)
+    else:
+        bound = 6.0 * 2.0 ** (int(w.kv_scale.max()) - 127)
+    assert float(o.abs().max()) <= bound * 1.01
