@@ -19,15 +19,18 @@
 // 2g + (piece starts before the range ? 0 : 1), and stage 2 merges those.  This
 // balances rows, not sequences, so ragged batches keep every CU equally busy.
 //
-// Stage-1 workgroup: 4 wave64s share an LDS ring of 32-row KV tiles filled by
-// 16-byte global->LDS DMA (buffer_load ... lds).  Per tile:
-//   QK : wave w computes S^T (16 tokens x 16 heads) for token block (w & 1)
-//        over dim half (w >> 1) with MFMA (K rows are the A operand, Q^T the
-//        B operand kept in registers); partial scores meet in LDS.
-//   softmax: every wave reads the 32 x 16 scores, keeps the running max in
-//        base 2 and forms P^T as the B operand of the next product.
-//   PV : wave w owns value columns [128w, 128w + 128): O^T += V^T P^T with V^T
-//        gathered from the same LDS tile (no second read of the row).
+// Stage-1 workgroup: four wave64s (two workgroups per CU, two waves per SIMD)
+// stream the 32-row KV tiles of a piece through a shared LDS ring filled by
+// 16-byte global->LDS DMA.  Per tile, each wave:
+//   QK : S^T (32 tokens x 16 heads) = K Q^T on MFMA over all 576 dims, K from
+//        the LDS tile (A operand), Q^T held in registers (B operand); both
+//        waves compute the same scores, which costs less than exchanging them;
+//   softmax: base-2 online softmax; the head-wide max and the rescale of the
+//        accumulators run only when some score exceeds its running max;
+//   PV : O^T (the wave's 128 value columns x 16 heads) += V^T P^T, V^T
+//        gathered from the same LDS tile, P^T taken straight from the
+//        registers that hold S^T.
+// One barrier per tile publishes the tile and frees its ring slot.
 // fp8 / MXFP4 values are widened to bf16 in registers (exact); only fp8 x fp8
 // queries/keys use the fp8 matrix instruction directly.
 
@@ -48,11 +51,10 @@ constexpr int kHeads = 16;
 constexpr int kQK = 576;
 constexpr int kV = 512;
 constexpr int kTile = 32;  // KV rows per LDS tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kScaleRow = kQK / 32;  // MXFP4 scale bytes per row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
@@ -60,11 +62,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 enum Dt { DT_BF16 = MLA_DTYPE_BF16, DT_FP8 = MLA_DTYPE_FP8_E4M3FN, DT_MXFP4 = MLA_DTYPE_MXFP4 };
 
 // ---------------------------------------------------------------- geometry
+//
+// A tile is 32 consecutive KV rows.  The four waves of a workgroup stream the
+// tiles of a piece through a shared ring of kStages LDS slots; a slot holds the
+// tile's rows and, for MXFP4, one 1 KB chunk with the tile's E8M0 scale bytes.
+// Two workgroups share a CU.
 
 template <int KF>
 struct KvGeom;
@@ -84,16 +90,18 @@ struct KvGeom<DT_MXFP4> {
 template <int KF>
 struct Geom {
   static constexpr int kRow = KvGeom<KF>::kRow;
-  static constexpr int kRowBytes = kTile * kRow;  // row bytes of one tile
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kStages = KvGeom<KF>::kStages;
+  static constexpr int kRowBytes = kTile * kRow;       // row bytes of one tile
   static constexpr int kRowChunks = kRowBytes / 1024;  // one chunk = one wave DMA instruction
   static constexpr int kChunks = kRowChunks + KvGeom<KF>::kScaleChunks;
+  static constexpr int kMaxChunksPerWave = (kChunks + kWaves - 1) / kWaves;  // wave w issues chunks w, w + 4, ...
   static constexpr int kStageBytes = kChunks * 1024;
-  static constexpr int kStages = KvGeom<KF>::kStages;
-  static constexpr int kRingBytes = kStages * kStageBytes;
-  static constexpr int kScoreFloats = kWaves * kHeads * 16;
-  static constexpr int kLdsBytes = kRingBytes + kScoreFloats * 4;
-  static constexpr int kMaxChunksPerWave = (kChunks + kWaves - 1) / kWaves;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
   static_assert(kRowBytes % 1024 == 0, "a tile must fill whole DMA chunks");
+  static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU");
+  static_assert((kStages - 2) * kMaxChunksPerWave <= 63, "vmcnt range");
   __host__ __device__ static constexpr int chunks_of_wave(int w) { return (kChunks - w + kWaves - 1) / kWaves; }
 };
 
@@ -152,78 +160,225 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 
 __device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// s_waitcnt vmcnt(n) for a runtime n in [0, 31] (the immediate must be constant).
-__device__ inline void wait_vmcnt(int n) {
-#define MLA_VMCNT_CASE(k) \
-  case k:                 \
-    asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); \
-    break;
-  switch (n) {
-    MLA_VMCNT_CASE(0) MLA_VMCNT_CASE(1) MLA_VMCNT_CASE(2) MLA_VMCNT_CASE(3) MLA_VMCNT_CASE(4)
-    MLA_VMCNT_CASE(5) MLA_VMCNT_CASE(6) MLA_VMCNT_CASE(7) MLA_VMCNT_CASE(8) MLA_VMCNT_CASE(9)
-    MLA_VMCNT_CASE(10) MLA_VMCNT_CASE(11) MLA_VMCNT_CASE(12) MLA_VMCNT_CASE(13) MLA_VMCNT_CASE(14)
-    MLA_VMCNT_CASE(15) MLA_VMCNT_CASE(16) MLA_VMCNT_CASE(17) MLA_VMCNT_CASE(18) MLA_VMCNT_CASE(19)
-    MLA_VMCNT_CASE(20) MLA_VMCNT_CASE(21) MLA_VMCNT_CASE(22) MLA_VMCNT_CASE(23) MLA_VMCNT_CASE(24)
-    MLA_VMCNT_CASE(25) MLA_VMCNT_CASE(26) MLA_VMCNT_CASE(27) MLA_VMCNT_CASE(28) MLA_VMCNT_CASE(29)
-    MLA_VMCNT_CASE(30)
-    default:
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      break;
+__device__ inline float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Four bf16 values (two words) times inv -> E4M3 hi terms and E4M3 lo
+// terms of the remainders, four codes per word in element order.
+__device__ inline void split4(uint32_t w0, uint32_t w1, float inv, uint32_t& hi, uint32_t& lo) {
+  const float x0 = bf_lo(w0) * inv, x1 = bf_hi(w0) * inv, x2 = bf_lo(w1) * inv, x3 = bf_hi(w1) * inv;
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+  const float r0 = x0 - __builtin_amdgcn_cvt_f32_fp8(h, 0), r1 = x1 - __builtin_amdgcn_cvt_f32_fp8(h, 1);
+  const float r2 = x2 - __builtin_amdgcn_cvt_f32_fp8(h, 2), r3 = x3 - __builtin_amdgcn_cvt_f32_fp8(h, 3);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
+  hi = (uint32_t)h;
+  lo = (uint32_t)l;
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int N>
+__device__ inline void wait_vmcnt_clamped() {
+  wait_vmcnt<(N < 63 ? N : 63)>();
+}
+
+// Wait until at most k * CHUNKS DMA instructions of this wave are in flight,
+// k in [0, 5] (the tiles issued after the one needed may stay in flight).
+template <int CHUNKS>
+__device__ inline void wait_tiles_behind_n(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt_clamped<CHUNKS>(); break;
+    case 2: wait_vmcnt_clamped<2 * CHUNKS>(); break;
+    case 3: wait_vmcnt_clamped<3 * CHUNKS>(); break;
+    case 4: wait_vmcnt_clamped<4 * CHUNKS>(); break;
+    default: wait_vmcnt_clamped<5 * CHUNKS>(); break;
   }
-#undef MLA_VMCNT_CASE
+}
+
+// Same for a wave that issues `chunks` DMA instructions per tile, where
+// chunks is MAXC or MAXC - 1 (the tile's 1 KB chunks are dealt round robin).
+template <int MAXC>
+__device__ inline void wait_tiles_behind(int chunks, int k) {
+  if (chunks == MAXC)
+    wait_tiles_behind_n<MAXC>(k);
+  else
+    wait_tiles_behind_n<(MAXC > 1 ? MAXC - 1 : 1)>(k);
 }
 
 // Workgroup barrier that also drains this wave's LDS traffic; the memory
 // clobber keeps the compiler from moving LDS accesses across it.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // dword3 0x00020000: 32-bit data format, raw (unswizzled) addressing.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource: base, no stride, `bytes` records, dword3 0x00020000
+// (32-bit data format, unswizzled).  Reads at or past `bytes` return zero.
+__device__ inline i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-// 16 bytes per lane from rsrc+voff into LDS at lds_base + 16*lane.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)voff, 0, 0, 0);
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane
+// (lds_base wave-uniform).  Issued through inline asm on purpose: the compiler
+// would otherwise treat every later LDS read as dependent on this write and
+// wait for all DMA in flight, which serialises the tile ring.  Completion is
+// tracked explicitly with s_waitcnt vmcnt before a tile is read.  m0 is not
+// used for anything else in these kernels.
+__device__ inline void dma16(i32x4 r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// ---------------------------------------------------------------- LDS layout
+//
+// A tile row of kRow bytes is stored as kRow / 16 units of 16 bytes, with unit
+// u of row r placed at unit u ^ swz(r).  The XOR moves rows that would fall on
+// the same LDS banks (576-byte rows repeat the bank pattern every 4 rows,
+// 1152-byte rows every 2, 288-byte rows every 8) onto different banks for the
+// access patterns below, and costs nothing at read time: every read offset is
+// a per-lane constant plus an immediate.  The DMA realises the layout by
+// choosing, for each LDS slot, which global 16-byte unit it loads.
+
+template <int KF>
+struct Layout;
+template <>
+struct Layout<DT_FP8> {
+  static constexpr int kUnits = 36;
+  __host__ __device__ static constexpr int swz(int row) { return (row >> 2) & 3; }
+};
+template <>
+struct Layout<DT_BF16> {
+  static constexpr int kUnits = 72;
+  __host__ __device__ static constexpr int swz(int row) { return (row >> 1) & 3; }
+};
+template <>
+struct Layout<DT_MXFP4> {
+  static constexpr int kUnits = 18;
+  __host__ __device__ static constexpr int swz(int row) { return (row >> 3) & 1; }
+};
+
+// Global byte offset (within a tile) of the 16-byte unit the DMA puts in LDS slot s.
+template <int KF>
+__device__ inline uint32_t dma_src_offset(int s) {
+  constexpr int U = Layout<KF>::kUnits;
+  const int r = s / U, u = s - r * U;
+  return (uint32_t)(16 * (r * U + (u ^ Layout<KF>::swz(r))));
 }
 
 // ---------------------------------------------------------------- operands
+//
+// MFMA 16x16x32 (bf16) operand layouts: lane l holds, for the A operand, row
+// l & 15 and the eight reduction indices of group l >> 4; for the B operand,
+// column l & 15 and the same eight reduction indices; the result puts rows
+// 4 * (l >> 4) + r, r = 0..3, of column l & 15 in lane l.  Only the pairing of
+// A and B reduction indices matters, so the dims of a chunk can be laid out
+// freely as long as K and Q use the same layout.
 
-// K operand (A of S^T = K Q^T): 8 consecutive key dims [dim0, dim0+8) of tile row `row`, as bf16.
+// Tile row of the i-th token a lane of group g feeds to the PV product: the
+// tokens whose scores the same lane holds after S^T = K Q^T (rows 4g..4g+3 of
+// each 16-row block), so P^T needs no data movement.
+__device__ inline int pv_row(int g, int i) { return (i < 4) ? 4 * g + i : 12 + 4 * g + i; }
+constexpr int pv_row_base(int i) { return (i < 4) ? i : 12 + i; }  // pv_row(g, i) - 4g
+
+// Per-lane LDS byte offsets (within a tile) of the reads a lane (m, g) makes.
+//   k[blk][par]: K operand of chunk c of token block blk is at k[blk][c & 1] + kstep * (c >> 1)
+//   x[blk][e]  : fp8 x fp8 path, 16-byte half e of the 32 key bytes of chunk c is at x[blk][e] + 128 c
+//   v[h]       : V rows; row pv_row(g, i) column group q starts at v[(i & 3) >> 1] + vrow(i) + vstep * q
 template <int KF>
-__device__ inline bf16x8 load_k8(const uint8_t* st, int row, int dim0, int sdelta) {
+struct LaneOffs {
+  int k[2][2];
+  int x[2][2];
+  int v[2];
+
+  __device__ inline void init(int m, int g) {
+    constexpr int R = Geom<KF>::kRow;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int row = 16 * blk + m;
+      const int f = Layout<KF>::swz(row);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        if constexpr (KF == DT_FP8) {
+          // dims 32c + 8g + [0, 8): unit 2c + (g >> 1), byte 8 (g & 1)
+          k[blk][par] = row * R + 16 * ((2 * par + (g >> 1)) ^ f) + 8 * (g & 1);
+          // dims 128c + 32g + [0, 32): units 8c + 2g + e
+          x[blk][par] = row * R + 16 * (4 * (g >> 1) + ((2 * (g & 1) + par) ^ f));
+        } else if constexpr (KF == DT_BF16) {
+          // dims 32c + 8g + [0, 8) as bf16: unit 4c + g
+          k[blk][par] = row * R + 16 * (g ^ f);
+          x[blk][par] = 0;
+        } else {
+          // dims 32c + 8g + [0, 8) as E2M1 pairs: unit c, byte 4g
+          k[blk][par] = row * R + 16 * (par ^ f) + 4 * g;
+          x[blk][par] = 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = pv_row(g, 2 * h);  // any row with the same (i & 3) >> 1 has the same swizzle
+      const int f = Layout<KF>::swz(row);
+      if constexpr (KF == DT_FP8) {
+        // columns 128q + 8m + [0, 8): unit 8q + (m >> 1), byte 8 (m & 1)
+        v[h] = 4 * g * R + 16 * ((m >> 1) ^ f) + 8 * (m & 1);
+      } else if constexpr (KF == DT_BF16) {
+        // unit 16q + m
+        v[h] = 4 * g * R + 16 * (m ^ f);
+      } else {
+        // unit 4q + (m >> 2), byte 4 (m & 3)
+        v[h] = 4 * g * R + 16 * ((m >> 2) ^ f) + 4 * (m & 3);
+      }
+    }
+  }
+};
+
+// K operand: key dims [32c + 8g, 32c + 8g + 8) of token block blk, as bf16.
+template <int KF>
+__device__ inline bf16x8 load_k8(const uint8_t* st, const LaneOffs<KF>& lo, int blk, int c, int m, int sdelta) {
   if constexpr (KF == DT_BF16) {
-    return *(const bf16x8*)(st + row * Geom<KF>::kRow + 2 * dim0);
+    return *(const bf16x8*)(st + lo.k[blk][0] + 64 * c);
   } else if constexpr (KF == DT_FP8) {
-    return fp8x8_bf16(*(const u32x2*)(st + row * Geom<KF>::kRow + dim0));
+    return fp8x8_bf16(*(const u32x2*)(st + lo.k[blk][c & 1] + 64 * (c >> 1)));
   } else {
-    const uint32_t w = *(const uint32_t*)(st + row * Geom<KF>::kRow + dim0 / 2);
-    const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + row * kScaleRow + dim0 / 32];
+    const uint32_t w = *(const uint32_t*)(st + lo.k[blk][c & 1] + 32 * (c >> 1));
+    const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + c];
     return fp4x8_bf16(w, e8m0_f32(e));
   }
 }
 
-// V^T operands (A of O^T = V^T P^T) for tile rows 8g+i (i = 0..7) and value
-// columns c0 + j (j = 0..7): a[j] element i = V[8g+i][c0+j].  Rows at or past
-// `valid` are zeroed when MASK.
+// V^T operands (A of O^T = V^T P^T) for value columns 128q + 8m + j (j = 0..7):
+// a[j] element i = V[pv_row(g, i)][128q + 8m + j].  Rows at or past `valid`
+// are zero when MASK.
 template <int KF, bool MASK>
-__device__ inline void load_vt(const uint8_t* st, int g, int c0, int sdelta, int valid, bf16x8 a[8]) {
-  uint32_t r[8][4];  // r[j][p] = bf16 pair (row 8g+2p, row 8g+2p+1) of column c0+j
+__device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q, int m, int g, int sdelta, int valid,
+                               bf16x8 a[8]) {
+  constexpr int R = Geom<KF>::kRow;
+  uint32_t r[8][4];  // r[j][p] = bf16 pair (token 2p, token 2p+1) of column j
   if constexpr (KF == DT_FP8) {
     u32x2 x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      x[i] = *(const u32x2*)(st + (8 * g + i) * Geom<KF>::kRow + c0);
-      if (MASK && 8 * g + i >= valid) x[i] = u32x2{0u, 0u};
+      x[i] = *(const u32x2*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 128 * q);
+      if (MASK && pv_row(g, i) >= valid) x[i] = u32x2{0u, 0u};
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const u32x2 lo = x[2 * p], hi = x[2 * p + 1];
+      const u32x2 lo2 = x[2 * p], hi2 = x[2 * p + 1];
       // interleave the bytes of two rows: (row0.b0, row1.b0, row0.b1, row1.b1), ...
-      const uint32_t l01 = __builtin_amdgcn_perm(hi.x, lo.x, 0x05010400u);
-      const uint32_t l23 = __builtin_amdgcn_perm(hi.x, lo.x, 0x07030602u);
-      const uint32_t h01 = __builtin_amdgcn_perm(hi.y, lo.y, 0x05010400u);
-      const uint32_t h23 = __builtin_amdgcn_perm(hi.y, lo.y, 0x07030602u);
+      const uint32_t l01 = __builtin_amdgcn_perm(hi2.x, lo2.x, 0x05010400u);
+      const uint32_t l23 = __builtin_amdgcn_perm(hi2.x, lo2.x, 0x07030602u);
+      const uint32_t h01 = __builtin_amdgcn_perm(hi2.y, lo2.y, 0x05010400u);
+      const uint32_t h23 = __builtin_amdgcn_perm(hi2.y, lo2.y, 0x07030602u);
       r[0][p] = fp8x2_bf16<false>(l01);
       r[1][p] = fp8x2_bf16<true>(l01);
       r[2][p] = fp8x2_bf16<false>(l23);
@@ -234,26 +389,25 @@ __device__ inline void load_vt(const uint8_t* st, int g, int c0, int sdelta, int
       r[7][p] = fp8x2_bf16<true>(h23);
     }
   } else {
-    u32x4 x[8];  // row-wise bf16 of columns c0..c0+7
+    u32x4 x[8];  // row-wise bf16 of the 8 columns
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = 8 * g + i;
       if constexpr (KF == DT_BF16) {
-        x[i] = *(const u32x4*)(st + row * Geom<KF>::kRow + 2 * c0);
+        x[i] = *(const u32x4*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 256 * q);
       } else {
-        const uint32_t w = *(const uint32_t*)(st + row * Geom<KF>::kRow + c0 / 2);
-        const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + row * kScaleRow + c0 / 32];
+        const uint32_t w = *(const uint32_t*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 64 * q);
+        const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + pv_row(g, i) * kScaleRow + 4 * q + (m >> 2)];
         x[i] = __builtin_bit_cast(u32x4, fp4x8_bf16(w, e8m0_f32(e)));
       }
-      if (MASK && row >= valid) x[i] = u32x4{0u, 0u, 0u, 0u};
+      if (MASK && pv_row(g, i) >= valid) x[i] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const u32x4 lo = x[2 * p], hi = x[2 * p + 1];
+      const u32x4 lo2 = x[2 * p], hi2 = x[2 * p + 1];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        r[2 * q][p] = __builtin_amdgcn_perm(hi[q], lo[q], 0x05040100u);
-        r[2 * q + 1][p] = __builtin_amdgcn_perm(hi[q], lo[q], 0x07060302u);
+      for (int k = 0; k < 4; ++k) {
+        r[2 * k][p] = __builtin_amdgcn_perm(hi2[k], lo2[k], 0x05040100u);
+        r[2 * k + 1][p] = __builtin_amdgcn_perm(hi2[k], lo2[k], 0x07060302u);
       }
     }
   }
@@ -281,167 +435,301 @@ struct SplitParams {
 };
 
 // Query operand of S^T = K Q^T: lane (head = lane & 15, group = lane >> 4)
-// holds Q^T for the dims of its dim half in the same order as the K operand.
+// holds Q^T for all 576 dims, laid out like the K operand.  Three forms:
+//   fp8 q, fp8 KV  : the fp8 codes, multiplied by fp8 K on the fp8 matrix unit;
+//   bf16 q, fp8 KV : q / s_h split into two fp8 terms hi + lo with a per-head
+//                    power-of-two s_h (hi = E4M3(q / s_h), lo = E4M3(q / s_h - hi)).
+//                    A bf16 value has 8 significant bits and hi, lo carry 4 each,
+//                    so the split is exact except for elements far below the
+//                    head's maximum; K then feeds the fp8 matrix unit unconverted;
+//   otherwise      : bf16 (fp8 q widened exactly), multiplied by K widened to bf16.
 template <int QF, int KF>
 struct QOperand {
   static constexpr bool kFp8Mfma = (QF == DT_FP8 && KF == DT_FP8);
-  bf16x8 b[9];   // bf16 path: dims half*288 + 32c + 8g + [0,8)
-  i32x8 b8[2];   // fp8 path: dims half*288 + 128c + 32g + [0,32)
-  uint64_t bx;   // fp8 path: dims half*288 + 256 + 8g + [0,8)
+  static constexpr bool kHiLo = (QF == DT_BF16 && KF == DT_FP8);
+  static constexpr bool kByteK = kFp8Mfma || kHiLo;  // K used as raw fp8 bytes
+  bf16x8 b[18];    // bf16 form: dims 32c + 8g + [0, 8)
+  i32x8 b8[4];     // fp8 forms (hi term): dims 128c + 32g + [0, 32)
+  uint64_t bx[2];  //                      dims 512 + 32c + 8g + [0, 8)
+  i32x8 l8[4];     // split form, lo term
+  uint64_t lx[2];
+  float scale;     // per-head factor of the scores (s_h for the split form, else 1)
 
-  __device__ inline void load(const uint8_t* q, int64_t qrow, int half, int lane) {
+  __device__ inline void load(const uint8_t* q, int64_t qrow, int lane) {
     const int h = lane & 15, g = lane >> 4;
-    const int64_t base = (qrow * kHeads + h) * kQK + 288 * half;
+    const int64_t base = (qrow * kHeads + h) * kQK;
+    scale = 1.f;
     if constexpr (kFp8Mfma) {
-      b8[0] = *(const i32x8*)(q + base + 32 * g);
-      b8[1] = *(const i32x8*)(q + base + 128 + 32 * g);
-      bx = *(const uint64_t*)(q + base + 256 + 8 * g);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b8[c] = *(const i32x8*)(q + base + 128 * c + 32 * g);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) bx[c] = *(const uint64_t*)(q + base + 512 + 32 * c + 8 * g);
+    } else if constexpr (kHiLo) {
+      const uint16_t* qb = (const uint16_t*)q + base;
+      u32x4 raw[4][4];  // chunk c: 32 bf16 = 4 x 16 bytes
+      u32x4 rx[2];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) raw[c][k] = *(const u32x4*)(qb + 128 * c + 32 * g + 8 * k);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) rx[c] = *(const u32x4*)(qb + 512 + 32 * c + 8 * g);
+      // head-wide max |q| over the 576 dims (144 per lane, 4 lanes per head)
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(raw[c][k][e])), fabsf(bf_hi(raw[c][k][e]))));
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(rx[c][e])), fabsf(bf_hi(rx[c][e]))));
+      amax = fmaxf(amax, shfl_xor(amax, 16));
+      amax = fmaxf(amax, shfl_xor(amax, 32));
+      // s = smallest power of two with amax / s <= 448
+      const uint32_t tb = __builtin_bit_cast(uint32_t, amax * (1.0f / 448.0f));
+      int ex = (int)((tb >> 23) & 255u) + ((tb & 0x7fffffu) ? 1 : 0);
+      ex = amax > 0.f ? std::min(std::max(ex, 1), 253) : 127;
+      scale = __builtin_bit_cast(float, (uint32_t)ex << 23);
+      const float inv = __builtin_bit_cast(float, (uint32_t)(254 - ex) << 23);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x4 hw[2], lw[2];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            uint32_t hv, lv;
+            split4(raw[c][k][e], raw[c][k][e + 1], inv, hv, lv);
+            hw[k >> 1][2 * (k & 1) + (e >> 1)] = hv;
+            lw[k >> 1][2 * (k & 1) + (e >> 1)] = lv;
+          }
+        b8[c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(hw[0], hw[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        l8[c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lw[0], lw[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint32_t h0, l0, h1, l1;
+        split4(rx[c][0], rx[c][1], inv, h0, l0);
+        split4(rx[c][2], rx[c][3], inv, h1, l1);
+        bx[c] = (uint64_t)h0 | ((uint64_t)h1 << 32);
+        lx[c] = (uint64_t)l0 | ((uint64_t)l1 << 32);
+      }
     } else if constexpr (QF == DT_BF16) {
 #pragma unroll
-      for (int c = 0; c < 9; ++c) b[c] = *(const bf16x8*)(q + 2 * (base + 32 * c + 8 * g));
+      for (int c = 0; c < 18; ++c) b[c] = *(const bf16x8*)(q + 2 * (base + 32 * c + 8 * g));
     } else {
 #pragma unroll
-      for (int c = 0; c < 9; ++c) b[c] = fp8x8_bf16(*(const u32x2*)(q + base + 32 * c + 8 * g));
+      for (int c = 0; c < 18; ++c) b[c] = fp8x8_bf16(*(const u32x2*)(q + base + 32 * c + 8 * g));
+    }
+  }
+
+  // Makes the compiler complete the query loads at this point.
+  __device__ inline void settle() {
+    if constexpr (kByteK) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(b8[c]));
+      asm volatile("" ::"v"(bx[0]), "v"(bx[1]));
+      if constexpr (kHiLo) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(l8[c]));
+        asm volatile("" ::"v"(lx[0]), "v"(lx[1]));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 18; ++c) asm volatile("" ::"v"(b[c]));
     }
   }
 };
 
+// S^T for the two 16-token blocks of a tile: s[blk][r] = score of token
+// 16 * blk + 4g + r for head lane & 15 (before scaling).  Two independent
+// accumulation chains keep the matrix pipe busy.
 template <int QF, int KF>
-__device__ inline f32x4 qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, int row, int half, int g,
-                                int sdelta) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (QOperand<QF, KF>::kFp8Mfma) {
-    const uint8_t* rp = st + row * Geom<KF>::kRow + 288 * half;
+__device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo, int m,
+                               int sdelta, f32x4 s[2]) {
+  s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  s[1] = s[0];
+  if constexpr (QOperand<QF, KF>::kByteK) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const u32x4 k0 = *(const u32x4*)(st + lo.x[blk][0] + 128 * c);
+        const u32x4 k1 = *(const u32x4*)(st + lo.x[blk][1] + 128 * c);
+        const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+        // formats 0/0 = fp8 E4M3 for both operands; scale exponents 127 = 2^0
+        s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.b8[c], s[blk], 0, 0, 0, 127, 0, 127);
+        if constexpr (QOperand<QF, KF>::kHiLo)
+          s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.l8[c], s[blk], 0, 0, 0, 127, 0, 127);
+      }
+      // at most two chunks of K operands live at a time
+      if (c & 1) __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const i32x8 k = *(const i32x8*)(rp + 128 * c + 32 * g);
-      // formats 0/0 = fp8 E4M3 for both operands; scale exponents 127 = 2^0
-      s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.b8[c], s, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        // dims 512 + 32c + 8g + [0, 8) sit where the bf16 path's chunk 16 + c does
+        const uint64_t k = *(const uint64_t*)(st + lo.k[blk][c & 1] + 512);
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.bx[c], s[blk], 0, 0, 0);
+        if constexpr (QOperand<QF, KF>::kHiLo)
+          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.lx[c], s[blk], 0, 0, 0);
+      }
     }
-    const uint64_t kx = *(const uint64_t*)(rp + 256 + 8 * g);
-    s = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)kx, (long)qo.bx, s, 0, 0, 0);
   } else {
 #pragma unroll
-    for (int c = 0; c < 9; ++c) {
-      const bf16x8 k = load_k8<KF>(st, row, 288 * half + 32 * c + 8 * g, sdelta);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qo.b[c], s, 0, 0, 0);
+    for (int c = 0; c < 18; ++c) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const bf16x8 k = load_k8<KF>(st, lo, blk, c, m, sdelta);
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qo.b[c], s[blk], 0, 0, 0);
+      }
+      // keep a few chunks of K in flight, not all 36 operands
+      if (c % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
   }
-  return s;
+}
+
+// Softmax state of one piece, identical in the four waves of the workgroup
+// except for acc: running max (base 2) per head, the lane's part of the
+// running sum, and O^T for the wave's 128 value columns: acc[j][r] = column
+// 128w + 32g + 8r + j of head lane & 15.
+struct WaveState {
+  float m_run;
+  float l_run;
+  f32x4 acc[8];
+};
+
+template <int QF, int KF, bool MASK>
+__device__ inline void process_tile(const uint8_t* st, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo,
+                                    WaveState& ws, int w, int m, int g, int sdelta, int valid, float score_scale) {
+  f32x4 s[2];
+  qk_tile<QF, KF>(st, qo, lo, m, sdelta, s);
+  float t[8];
+  float mx = -INFINITY;
+  const float sc = score_scale * qo.scale;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    t[k] = s[k >> 2][k & 3] * sc;
+    if (MASK && pv_row(g, k) >= valid) t[k] = -INFINITY;
+    mx = fmaxf(mx, t[k]);
+  }
+  // The reference max m_run is raised (to the exact head-wide maximum) and the
+  // accumulators rescaled only when a score exceeds it by more than
+  // kRescaleSlack; otherwise p = 2^(t - m_run) <= 2^kRescaleSlack, which bf16
+  // P and the fp32 sums hold without loss, and the final normalisation by the
+  // running sum is unchanged.  Both waves see the same scores, so they take
+  // the same decisions.
+  if (__builtin_amdgcn_ballot_w64(mx > ws.m_run + kRescaleSlack) != 0) {
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(ws.m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
+    ws.m_run = m_new;
+    ws.l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ws.acc[j] *= alpha;
+  }
+  uint32_t pk[4];
+  float ps = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float p0 = __builtin_amdgcn_exp2f(t[2 * k] - ws.m_run);
+    const float p1 = __builtin_amdgcn_exp2f(t[2 * k + 1] - ws.m_run);
+    ps += p0 + p1;
+    pk[k] = pack_bf16x2(p0, p1);
+  }
+  ws.l_run += ps;
+  const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+  bf16x8 va[8];
+  load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ws.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, ws.acc[j], 0, 0, 0);
 }
 
 template <int QF, int KF>
-__device__ void split_piece(const SplitParams& p, uint8_t* ring, float* sx, int64_t qrow, int64_t r0, int n,
-                            int32_t slot, float score_scale, float out_scale) {
+__device__ void split_piece(const SplitParams& p, uint8_t* ring, int64_t qrow, int64_t r0, int n, int32_t slot,
+                            float score_scale, float out_scale) {
   using G = Geom<KF>;
   constexpr int NS = G::kStages;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int m = lane & 15;
-  const int half = w >> 1;
   const int ntiles = (n + kTile - 1) / kTile;
 
   // Buffer resources: rows from r0 on (reads past the buffer return zero).
   const uint8_t* kv_base = p.kv + r0 * G::kRow;
   const uint64_t kv_avail = (uint64_t)(p.total_kv - r0) * G::kRow;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_base, (uint32_t)std::min<uint64_t>(kv_avail, 0xFFFFF000ull));
+  const i32x4 rk = make_rsrc(kv_base, (uint32_t)std::min<uint64_t>(kv_avail, 0xFFFFF000ull));
   int64_t sbase = 0;
-  __amdgpu_buffer_rsrc_t rs = rk;
+  i32x4 rs = rk;
   if constexpr (KF == DT_MXFP4) {
     sbase = (r0 * kScaleRow) & ~(int64_t)15;
     const uint64_t sbytes = (((uint64_t)p.total_kv * kScaleRow + 15) & ~15ull) - (uint64_t)sbase;
     rs = make_rsrc(p.kv_scale + sbase, (uint32_t)std::min<uint64_t>(sbytes, 0xFFFFF000ull));
   }
 
+  // Tile t goes to slot t % NS; wave w issues the chunks c = w, w + 4, ...
+  // Lane offsets of its row chunks follow the swizzled layout.
+  uint32_t src[G::kMaxChunksPerWave];
+#pragma unroll
+  for (int k = 0; k < G::kMaxChunksPerWave; ++k) {
+    const int c = w + G::kWaves * k;
+    src[k] = c < G::kRowChunks ? dma_src_offset<KF>(64 * c + lane) : 0u;
+  }
   auto issue_tile = [&](int t) {
-    uint8_t* stage = ring + (t % NS) * G::kStageBytes;
+    const uint8_t* stage = ring + (t % NS) * G::kStageBytes;
 #pragma unroll
     for (int k = 0; k < G::kMaxChunksPerWave; ++k) {
-      const int c = w + kWaves * k;
+      const int c = w + G::kWaves * k;
+      if (c >= G::kChunks) break;
       if (c < G::kRowChunks) {
-        dma16(rk, stage + c * 1024, (uint32_t)(t * G::kRowBytes + c * 1024 + lane * 16));
-      } else if (c < G::kChunks) {
+        dma16(rk, uniform(lds_addr(stage + c * 1024)), (uint32_t)(t * G::kRowBytes) + src[k]);
+      } else {
         const int64_t a = ((r0 + (int64_t)t * kTile) * kScaleRow) & ~(int64_t)15;
-        dma16(rs, stage + G::kRowBytes, (uint32_t)(a - sbase) + lane * 16);
+        dma16(rs, uniform(lds_addr(stage + G::kRowBytes)), (uint32_t)(a - sbase) + lane * 16);
       }
     }
   };
 
-  QOperand<QF, KF> qop;
-  qop.load(p.q, qrow, half, lane);
+  LaneOffs<KF> lo;
+  lo.init(m, g);
 
+  QOperand<QF, KF> qop;
+  qop.load(p.q, qrow, lane);
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
+  // Make the compiler complete the query loads here (its wait also covers the
+  // prologue DMA issued after them); otherwise it would place those waits in
+  // the tile loop, where they would drain the whole DMA ring every tile.
+  qop.settle();
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[8];
+  WaveState ws;
+  ws.m_run = -INFINITY;
+  ws.l_run = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 8; ++j) ws.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int cnt_w = G::chunks_of_wave(w);
+  const int my_chunks = G::chunks_of_wave(w);
   for (int i = 0; i < ntiles; ++i) {
-    wait_vmcnt(std::min(NS - 2, ntiles - 1 - i) * cnt_w);
-    lds_barrier();  // tile i complete in LDS; every wave is done with tile i-1
+    wait_tiles_behind<G::kMaxChunksPerWave>(my_chunks, std::min(NS - 2, ntiles - 1 - i));
+    lds_barrier();  // tile i is complete in LDS; both waves are done with tile i - 1
     if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
-
     const uint8_t* st = ring + (i % NS) * G::kStageBytes;
     const int valid = std::min(kTile, n - i * kTile);
     const int sdelta = (KF == DT_MXFP4) ? (int)(((r0 + (int64_t)i * kTile) * kScaleRow) & 15) : 0;
-
-    // ---- S^T partial for token block (w & 1), dim half (w >> 1)
-    const f32x4 s = qk_tile<QF, KF>(st, qop, 16 * (w & 1) + m, half, g, sdelta);
-    *(f32x4*)(sx + (w * kHeads + m) * 16 + 4 * g) = s;
-    lds_barrier();
-
-    // ---- online softmax (base 2) for tokens 8g..8g+7 of head m
-    const int bb = g >> 1, tb = 8 * (g & 1);
-    const f32x4 a0 = *(const f32x4*)(sx + (bb * kHeads + m) * 16 + tb);
-    const f32x4 a1 = *(const f32x4*)(sx + (bb * kHeads + m) * 16 + tb + 4);
-    const f32x4 b0 = *(const f32x4*)(sx + ((bb + 2) * kHeads + m) * 16 + tb);
-    const f32x4 b1 = *(const f32x4*)(sx + ((bb + 2) * kHeads + m) * 16 + tb + 4);
-    float t[8] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w,
-                  a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
-    const bool tail = valid < kTile;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      t[k] *= score_scale;
-      if (tail && 8 * g + k >= valid) t[k] = -INFINITY;
-      mx = fmaxf(mx, t[k]);
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float ps = 0.f;
-    uint32_t pk[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float p0 = __builtin_amdgcn_exp2f(t[2 * k] - m_new);
-      const float p1 = __builtin_amdgcn_exp2f(t[2 * k + 1] - m_new);
-      ps += p0 + p1;
-      pk[k] = pack_bf16x2(p0, p1);
-    }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-
-    // ---- O^T += V^T P^T over value columns [128w, 128w+128)
-    bf16x8 va[8];
-    if (tail)
-      load_vt<KF, true>(st, g, 128 * w + 8 * m, sdelta, valid, va);
+    if (valid < kTile)
+      process_tile<QF, KF, true>(st, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
     else
-      load_vt<KF, false>(st, g, 128 * w + 8 * m, sdelta, valid, va);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[j] *= alpha;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, acc[j], 0, 0, 0);
-    }
+      process_tile<QF, KF, false>(st, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
   }
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
-  float lt = l_run + shfl_xor(l_run, 16);
+  float lt = ws.l_run + shfl_xor(ws.l_run, 16);
   lt += shfl_xor(lt, 32);
   const float inv = out_scale / lt;
   const int col0 = 128 * w + 32 * g;
@@ -451,27 +739,26 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* sx, int6
     for (int r = 0; r < 4; ++r) {
       u32x4 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(acc[2 * q][r] * inv, acc[2 * q + 1][r] * inv);
+      for (int k = 0; k < 4; ++k) v[k] = pack_bf16x2(ws.acc[2 * k][r] * inv, ws.acc[2 * k + 1][r] * inv);
       *(u32x4*)(o + 8 * r) = v;
     }
   } else {
     float* o = p.part_o + ((int64_t)slot * kHeads + m) * kV + col0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      f32x4 v0 = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
-      f32x4 v1 = {acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
-      *(f32x4*)(o + 8 * r) = v0;
-      *(f32x4*)(o + 8 * r + 4) = v1;
+      *(f32x4*)(o + 8 * r) = f32x4{ws.acc[0][r] * inv, ws.acc[1][r] * inv, ws.acc[2][r] * inv, ws.acc[3][r] * inv};
+      *(f32x4*)(o + 8 * r + 4) = f32x4{ws.acc[4][r] * inv, ws.acc[5][r] * inv, ws.acc[6][r] * inv, ws.acc[7][r] * inv};
     }
-    if (w == 0 && g == 0) p.part_lse[(int64_t)slot * kHeads + m] = (m_run + __builtin_amdgcn_logf(lt)) * kLn2;
   }
+  if (slot >= 0 && w == 0 && g == 0)
+    p.part_lse[(int64_t)slot * kHeads + m] = (ws.m_run + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
 template <int QF, int KF>
-__global__ __launch_bounds__(kThreads, 2) void mla_split_kernel(SplitParams p) {
+__global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_split_kernel(
+    SplitParams p) {
   using G = Geom<KF>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[G::kRingBytes];
-  __shared__ __attribute__((aligned(16))) float sx[G::kScoreFloats];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[G::kLdsBytes];
   __shared__ int counts[2];
 
   const int tid = threadIdx.x;
@@ -484,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_split_kernel(SplitParams p) {
   if (tid < 2) counts[tid] = 0;
   __syncthreads();
   int c_first = 0, c_end = 0;
-  for (int j = tid; j <= p.batch; j += kThreads) {
+  for (int j = tid; j <= p.batch; j += G::kThreads) {
     const int64_t v = p.kv_indptr[j];
     c_first += (j >= 1 && v <= lo);
     c_end += (j < p.batch && v < hi);
@@ -514,8 +801,8 @@ __global__ __launch_bounds__(kThreads, 2) void mla_split_kernel(SplitParams p) {
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
     const int64_t qrow = std::min(std::max(uniform(p.qo_indptr[b]), 0), p.total_q - 1);
-    split_piece<QF, KF>(p, ring, sx, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale);
-    lds_barrier();  // the next piece reuses the ring and the score exchange
+    split_piece<QF, KF>(p, ring, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale);
+    lds_barrier();  // the next piece refills the ring
   }
 }
 
@@ -650,7 +937,7 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 template <int QF, int KF>
 hipError_t launch_split(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
-  hipLaunchKernelGGL((mla_split_kernel<QF, KF>), dim3(pl->num_wgs), dim3(kThreads), 0, st, sp);
+  hipLaunchKernelGGL((mla_split_kernel<QF, KF>), dim3(pl->num_wgs), dim3(Geom<KF>::kThreads), 0, st, sp);
   return hipGetLastError();
 }
 
