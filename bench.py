@@ -1,7 +1,8 @@
 """MLA decode benchmark on one MI355X.
 
-A step is one mla_decode_run-equivalent call (stage 1 split kernel + stage 2
-LSE merge) over one batch of seeded synthetic inputs already resident in HBM.
+A step is one decode of the batch (mla_decode_split, the stage-1 split
+kernel, then mla_decode_merge, the stage-2 LSE merge - together what
+mla_decode_run launches) over seeded synthetic inputs already resident in HBM.
 The default workload is bs=64, kv_len=8192, bf16 q, fp8 E4M3FN KV (the
 bs>=32 / kv=8192 / fp8 shape the bandwidth target is stated for).  The KV
 buffer is rotated over enough copies (>= 768 MB in total) that each call reads
@@ -30,6 +31,21 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "bs64_kv8192_fp8"
+KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip")
+
+# HBM bytes of one stage-1 launch on the default workload, from two rocprofv3
+# counter passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
+# what the same counter reads for a plain device copy of 512 MiB.  Valid only
+# for the kernel source they were taken on (its sha256); otherwise traffic is
+# reported as null.
+TRAFFIC_MEASURED = {
+    "workload": DEFAULT_WORKLOAD,
+    "source_sha256": "cf98729a3a54230e0639c79a9de520399c4a66bd4b524cb55ccdc8d21f9437d4",
+    "fetch_kib": 153019.86,
+    "write_kib": 21148.49,
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
+}
 
 
 def _args():
@@ -43,6 +59,9 @@ def _args():
     ap.add_argument("--hot", action="store_true", help="no KV rotation (cache-resident numbers, secondary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only-headline", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MB (reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -79,6 +98,98 @@ def cpu_baseline(w, kv_bytes_per_row: float, target_s: float) -> dict:
             "sample": f"{len(take)} of {len(lengths)} sequences ({rows} KV rows), fp64 C, {dt:.2f} s wall"}
 
 
+def _source_sha256() -> str:
+    import hashlib
+
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _measured_traffic(name: str):
+    t = TRAFFIC_MEASURED
+    if name != t["workload"] or not t["source_sha256"] or t["source_sha256"] != _source_sha256():
+        return None
+    return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
+
+
+class Timed:
+    """One workload resident on the GPU, its plan and rotated KV copies."""
+
+    def __init__(self, name, args, threads):
+        import torch
+        import synth
+        from mla_decode_split_amd import device as dev
+
+        self.name = name
+        self.spec = synth.WORKLOADS[name]
+        t = time.perf_counter()
+        self.w = synth.make_workload(name, threads=threads)
+        self.t_gen = time.perf_counter() - t
+        self.kv_bytes = self.w.kv_bytes()
+        self.rows = int(self.w.kv_indptr[-1] - self.w.kv_indptr[0])
+        self.batch = dev.upload(self.w)
+        t = time.perf_counter()
+        self.plan = dev.plan_for(self.batch, rows_per_split=args.rows_per_split, wgs_per_cu=args.wgs_per_cu)
+        self.t_plan = time.perf_counter() - t
+        self.ncopy = 1 if args.hot else max(1, min(8, math.ceil(768e6 / max(self.kv_bytes, 1))))
+        self.kvs = [self.batch.kv] + [self.batch.kv.clone() for _ in range(self.ncopy - 1)]
+        self.out = torch.empty((self.batch.total_q, 16, 512), dtype=torch.bfloat16, device="cuda")
+        self.ws = dev.workspace_for(self.plan)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i, ev=None):
+        from mla_decode_split_amd import device as dev
+
+        self.batch.kv = self.kvs[i % self.ncopy]
+        if ev is not None:
+            ev[0].record(self.stream)
+        dev.run_split(self.plan, self.batch, self.out, self.ws, self.stream)  # stage 1, timed by the events
+        if ev is not None:
+            ev[1].record(self.stream)
+        dev.run_merge(self.plan, self.batch, self.out, self.ws, self.stream)
+
+    def time(self, steps, warmup, per_launch=True):
+        import torch
+
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i, evs[i] if per_launch else None)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        split_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs])) if per_launch else None
+        return elapsed, split_us
+
+    def read_ceiling(self, reps=20):
+        """GB/s of the plain read kernel over the same rotated KV copies."""
+        import torch
+        import mla_decode_split_amd as mla
+
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        nbytes = self.kv_bytes // 16 * 16 if self.w.kv_dtype != "mxfp4" else self.kvs[0].numel() // 16 * 16
+        for i in range(3):
+            mla.mla_debug_stream_read(self.kvs[i % self.ncopy], nbytes, sink, self.stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for i in range(reps):
+            mla.mla_debug_stream_read(self.kvs[i % self.ncopy], nbytes, sink, self.stream)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+    def describe(self):
+        import mla_decode_split_amd as mla
+
+        d = mla.mla_decode_plan_describe(self.plan)
+        return {"workload": self.name, "batch_size": self.spec["bs"], "kv_len": self.spec["kv_len"],
+                "q_dtype": self.w.q_dtype, "kv_dtype": self.w.kv_dtype, "kv_rows": self.rows,
+                "kv_bytes": self.kv_bytes, "kv_copies_rotated": self.ncopy, "num_splits": d["num_splits"],
+                "rows_per_split": d["rows_per_split"], "stage2": bool(d["stage2"])}
+
+
 def main() -> int:
     args = _args()
     if args.gpus != 1:
@@ -89,54 +200,21 @@ def main() -> int:
     import torch
 
     import mla_decode_split_amd as mla
-    from mla_decode_split_amd import device as dev
-    import synth
 
     if not os.path.exists(mla.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
     torch.cuda.set_device(0)
+    threads = _host_threads()
     name = args.workload
-    spec = synth.WORKLOADS[name]
-    t_gen = time.perf_counter()
-    w = synth.make_workload(name, threads=_host_threads())
-    t_gen = time.perf_counter() - t_gen
-    kv_bytes = w.kv_bytes()
-    rows = int(w.kv_indptr[-1] - w.kv_indptr[0])
-    bpr = kv_bytes / rows
 
-    batch = dev.upload(w)
-    plan = dev.plan_for(batch, rows_per_split=args.rows_per_split, wgs_per_cu=args.wgs_per_cu)
-    desc = mla.mla_decode_plan_describe(plan)
-    ncopy = 1 if args.hot else max(1, min(8, math.ceil(768e6 / max(kv_bytes, 1))))
-    kvs = [batch.kv] + [batch.kv.clone() for _ in range(ncopy - 1)]
-    out = torch.empty((batch.total_q, 16, 512), dtype=torch.bfloat16, device="cuda")
-    ws = dev.workspace_for(plan)
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        batch.kv = kvs[i % ncopy]
-        if ev is not None:
-            ev[0].record(stream)
-        dev.run_split(plan, batch, out, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        dev.run_merge(plan, batch, out, ws, stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    split_ms = [a.elapsed_time(b) for a, b in evs]
-    split_us = 1e3 * float(np.mean(split_ms))
+    h = Timed(name, args, threads)
+    elapsed, split_us = h.time(args.steps, args.warmup)
     ms_per_step = 1e3 * elapsed / args.steps
-    value = kv_bytes * args.steps / elapsed / 1e9
-    achieved = kv_bytes / (split_us * 1e-6) / 1e9
+    value = h.kv_bytes * args.steps / elapsed / 1e9
+    achieved = h.kv_bytes / (split_us * 1e-6) / 1e9
+    ceiling = h.read_ceiling()
+    cfg = h.describe()
 
     res = {
         "metric": "MLA decode achieved HBM bandwidth on KV bytes (stage 1 + stage 2 per call)",
@@ -148,23 +226,49 @@ def main() -> int:
         "ms_per_step": round(ms_per_step, 5),
         "us_per_call": round(1e3 * ms_per_step, 2),
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "read_ceiling_GBs": round(ceiling, 1),
+        "frac_of_read_ceiling": round(value / ceiling, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if (w.q_dtype == "fp8" and w.kv_dtype == "fp8") else "bf16",
+        "dtype": "fp8" if (h.w.q_dtype == "fp8" and h.w.kv_dtype == "fp8") else "bf16",
         "data": "synthetic (seeded N(0,1), quantised per the workload's KV format)",
-        "config": {"workload": name, "batch_size": spec["bs"], "kv_len": spec["kv_len"], "q_dtype": w.q_dtype,
-                   "kv_dtype": w.kv_dtype, "kv_rows": rows, "kv_bytes": kv_bytes,
-                   "kv_copies_rotated": ncopy, "num_splits": desc["num_splits"],
-                   "rows_per_split": desc["rows_per_split"], "stage2": bool(desc["stage2"])},
+        "config": cfg,
         "roofline": {"bound": "hbm", "kernel": "mla_split_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(split_us, 3),
-                     "bytes_per_launch": kv_bytes},
-        "input_generation_s": round(t_gen, 2),
+                     "traffic": _measured_traffic(name), "avg_launch_us": round(split_us, 3),
+                     "bytes_per_launch": h.kv_bytes},
+        "plan_us": round(1e6 * h.t_plan, 1),
+        "input_generation_s": round(h.t_gen, 2),
     }
+    if args.copy_calibration_mb > 0:
+        src = torch.empty(args.copy_calibration_mb << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = int(src.numel())
+    w_head, bpr = h.w, h.kv_bytes / h.rows
+    del h
+    if not args.only_headline:
+        import synth
+
+        table = []
+        for other in synth.WORKLOADS:
+            t = Timed(other, args, threads)
+            el, _ = t.time(args.steps, args.warmup, per_launch=False)
+            us = 1e6 * el / args.steps
+            d = t.describe()
+            table.append({"workload": other, "us_per_call": round(us, 2),
+                          "GBs": round(t.kv_bytes / (us * 1e-6) / 1e9, 1),
+                          "frac_of_peak": round(t.kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "kv_bytes": t.kv_bytes, "num_splits": d["num_splits"],
+                          "rows_per_split": d["rows_per_split"], "stage2": d["stage2"]})
+            del t
+            torch.cuda.empty_cache()
+        res["workloads"] = table
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, bpr, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w_head, bpr, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 

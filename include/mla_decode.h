@@ -188,6 +188,18 @@ mla_status mla_decode_plan_merge_slots(const mla_plan* plan, const int32_t* kv_i
 mla_status mla_debug_decode(int32_t kv_dtype, const void* codes, const void* scales, float* out, int64_t n,
                             void* stream);
 
+/*
+ * Read-bandwidth reference for reports (not part of the decode): one launch
+ * that reads `bytes` of device memory at `buf` with plain 16-byte loads and
+ * nothing else, so that timing it gives the HBM read rate this device
+ * sustains, against which the decode's rate can be set.
+ *   buf    device, 16-byte aligned; bytes a multiple of 16 (MLA_ERR_INVALID_ARG otherwise).
+ *   sink   device uint32[1]; written only in the (practically impossible) case that
+ *          the XOR of everything read equals 0x9E3779B9.
+ * Asynchronous on `stream`.
+ */
+mla_status mla_debug_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Human-readable status name. */
 const char* mla_status_string(mla_status status);
 

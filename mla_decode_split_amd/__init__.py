@@ -77,6 +77,8 @@ def _lib_handle():
         lib.mla_decode_plan_merge_slots.restype = i32
         lib.mla_debug_decode.argtypes = [i32, vp, vp, vp, i64, vp]
         lib.mla_debug_decode.restype = i32
+        lib.mla_debug_stream_read.argtypes = [vp, i64, vp, vp]
+        lib.mla_debug_stream_read.restype = i32
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_last_error_string.argtypes = []
@@ -229,3 +231,9 @@ def mla_debug_decode(kv_dtype, codes, scales, out, n: int, stream=None) -> None:
                                         _stream(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_debug_decode")
+
+
+def mla_debug_stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    st = _lib_handle().mla_debug_stream_read(_addr(buf), nbytes, _addr(sink), _stream(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_debug_stream_read")

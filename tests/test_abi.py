@@ -186,6 +186,10 @@ def test_run_argument_errors_before_any_launch():
     assert mla.library().mla_decode_run(None, A, A, A, A, A, A, A, A, 1 << 30, None) == mla.MLA_ERR_INVALID_ARG
     assert mla.library().mla_debug_decode(7, A, A, A, 10, None) == mla.MLA_ERR_UNSUPPORTED
     assert mla.library().mla_debug_decode(2, A, None, A, 10, None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.library().mla_debug_stream_read(A, 24, A, None) == mla.MLA_ERR_INVALID_ARG   # not 16-byte sized
+    assert mla.library().mla_debug_stream_read(A + 8, 32, A, None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.library().mla_debug_stream_read(A, 32, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.library().mla_debug_stream_read(A, 0, A, None) == mla.MLA_OK                 # nothing to launch
 
 
 def test_plan_destroy_accepts_null():
