@@ -100,7 +100,7 @@ struct Geom {
   static constexpr int kStageBytes = kChunks * 1024;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static_assert(kRowBytes % 1024 == 0, "a tile must fill whole DMA chunks");
-  static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU");
+  static_assert(2 * (kLdsBytes + 4 * 2 * 64 * 16) <= 160 * 1024, "two workgroups per CU (ring + score exchange)");
   static_assert((kStages - 2) * kMaxChunksPerWave <= 63, "vmcnt range");
   __host__ __device__ static constexpr int chunks_of_wave(int w) { return (kChunks - w + kWaves - 1) / kWaves; }
 };
@@ -290,17 +290,25 @@ __device__ inline uint32_t dma_src_offset(int s) {
 __device__ inline int pv_row(int g, int i) { return (i < 4) ? 4 * g + i : 12 + 4 * g + i; }
 constexpr int pv_row_base(int i) { return (i < 4) ? i : 12 + i; }  // pv_row(g, i) - 4g
 
-// Per-lane LDS byte offsets (within a tile) of the reads a lane (m, g) makes.
+// Per-lane LDS byte offsets (within a tile) of the reads a lane (m, g) of
+// wave w makes.
 //   k[blk][par]: K operand of chunk c of token block blk is at k[blk][c & 1] + kstep * (c >> 1)
 //   x[blk][e]  : fp8 x fp8 path, 16-byte half e of the 32 key bytes of chunk c is at x[blk][e] + 128 c
 //   v[h]       : V rows; row pv_row(g, i) column group q starts at v[(i & 3) >> 1] + vrow(i) + vstep * q
+// and the same with this wave's share of the dims folded in:
+//   xw[blk][e] : x[blk][e] + 128 w (main chunk w of the fp8 x fp8 path)
+//   kr[blk]    : rope chunk w (waves 0, 1) of the fp8 x fp8 path
+//   kb[blk]    : bf16 / MXFP4 path, chunk w + 4k is at kb[blk] + kbstep * k
 template <int KF>
 struct LaneOffs {
   int k[2][2];
   int x[2][2];
   int v[2];
+  int xw[2][2];
+  int kr[2];
+  int kb[2];
 
-  __device__ inline void init(int m, int g) {
+  __device__ inline void init(int m, int g, int w) {
     constexpr int R = Geom<KF>::kRow;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -324,6 +332,26 @@ struct LaneOffs {
         }
       }
     }
+    // the same formulas as k[][] with par = w & 1 (computed, not selected, so
+    // that the offsets stay in registers)
+    const int par = w & 1;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int row = 16 * blk + m;
+      const int f = Layout<KF>::swz(row);
+      xw[blk][0] = x[blk][0] + 128 * w;
+      xw[blk][1] = x[blk][1] + 128 * w;
+      if constexpr (KF == DT_FP8) {
+        kr[blk] = row * R + 16 * ((2 * par + (g >> 1)) ^ f) + 8 * (g & 1) + 512;
+        kb[blk] = 0;
+      } else if constexpr (KF == DT_BF16) {
+        kr[blk] = 0;
+        kb[blk] = row * R + 16 * (g ^ f) + 64 * w;
+      } else {
+        kr[blk] = 0;
+        kb[blk] = row * R + 16 * (par ^ f) + 4 * g + 32 * (w >> 1);
+      }
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = pv_row(g, 2 * h);  // any row with the same (i & 3) >> 1 has the same swizzle
@@ -342,17 +370,17 @@ struct LaneOffs {
   }
 };
 
-// K operand: key dims [32c + 8g, 32c + 8g + 8) of token block blk, as bf16.
+// K operand of the bf16 path: key dims [32c + 8g, 32c + 8g + 8) of token
+// block blk, as bf16, for this wave's chunk c = w + 4k.
 template <int KF>
-__device__ inline bf16x8 load_k8(const uint8_t* st, const LaneOffs<KF>& lo, int blk, int c, int m, int sdelta) {
+__device__ inline bf16x8 load_kw(const uint8_t* st, const LaneOffs<KF>& lo, int blk, int k, int w, int m, int sdelta) {
   if constexpr (KF == DT_BF16) {
-    return *(const bf16x8*)(st + lo.k[blk][0] + 64 * c);
-  } else if constexpr (KF == DT_FP8) {
-    return fp8x8_bf16(*(const u32x2*)(st + lo.k[blk][c & 1] + 64 * (c >> 1)));
+    return *(const bf16x8*)(st + lo.kb[blk] + 256 * k);
   } else {
-    const uint32_t w = *(const uint32_t*)(st + lo.k[blk][c & 1] + 32 * (c >> 1));
-    const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + c];
-    return fp4x8_bf16(w, e8m0_f32(e));
+    static_assert(KF == DT_MXFP4, "fp8 keys use the byte path");
+    const uint32_t word = *(const uint32_t*)(st + lo.kb[blk] + 64 * k);
+    const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + w + 4 * k];
+    return fp4x8_bf16(word, e8m0_f32(e));
   }
 }
 
@@ -434,58 +462,59 @@ struct SplitParams {
   float sm_scale;
 };
 
-// Query operand of S^T = K Q^T: lane (head = lane & 15, group = lane >> 4)
-// holds Q^T for all 576 dims, laid out like the K operand.  Three forms:
+// Query operand of S^T = K Q^T for the dims this wave multiplies.  The four
+// waves of a workgroup split the 576 dims (each computes a partial S^T over
+// its share for all tokens of the tile; the partials are summed through LDS),
+// so every product is computed once.  Lane (head = lane & 15, group = lane >> 4)
+// holds, laid out like the K operand:
+//   byte-K forms: dims 128w + 32g + [0, 32) (one 16x16x128 chunk) and, for
+//                 waves 0 and 1, rope dims 512 + 32w + 8g + [0, 8);
+//   bf16 form   : dims 32c + 8g + [0, 8) of chunks c = w + 4k, k < 5, c < 18.
+// The three operand kinds:
 //   fp8 q, fp8 KV  : the fp8 codes, multiplied by fp8 K on the fp8 matrix unit;
-//   bf16 q, fp8 KV : q / s_h split into two fp8 terms hi + lo with a per-head
-//                    power-of-two s_h (hi = E4M3(q / s_h), lo = E4M3(q / s_h - hi)).
+//   bf16 q, fp8 KV : q / s split into two fp8 terms hi + lo with a power-of-two
+//                    s per (wave, head) (hi = E4M3(q / s), lo = E4M3(q / s - hi)).
 //                    A bf16 value has 8 significant bits and hi, lo carry 4 each,
 //                    so the split is exact except for elements far below the
-//                    head's maximum; K then feeds the fp8 matrix unit unconverted;
+//                    maximum the scale is chosen for; K then feeds the fp8 matrix
+//                    unit unconverted;
 //   otherwise      : bf16 (fp8 q widened exactly), multiplied by K widened to bf16.
 template <int QF, int KF>
 struct QOperand {
   static constexpr bool kFp8Mfma = (QF == DT_FP8 && KF == DT_FP8);
   static constexpr bool kHiLo = (QF == DT_BF16 && KF == DT_FP8);
   static constexpr bool kByteK = kFp8Mfma || kHiLo;  // K used as raw fp8 bytes
-  bf16x8 b[18];    // bf16 form: dims 32c + 8g + [0, 8)
-  i32x8 b8[4];     // fp8 forms (hi term): dims 128c + 32g + [0, 32)
-  uint64_t bx[2];  //                      dims 512 + 32c + 8g + [0, 8)
-  i32x8 l8[4];     // split form, lo term
-  uint64_t lx[2];
-  float scale;     // per-head factor of the scores (s_h for the split form, else 1)
+  static constexpr int kBfChunks = 5;
+  bf16x8 b[kBfChunks];  // bf16 form
+  i32x8 b8;             // fp8 forms (hi term): main chunk
+  uint64_t bx;          //                      rope chunk (waves 0, 1)
+  i32x8 l8;             // split form, lo term
+  uint64_t lx;
+  float scale;          // factor of this wave's partial scores (s for the split form, else 1)
 
-  __device__ inline void load(const uint8_t* q, int64_t qrow, int lane) {
+  __device__ inline void load(const uint8_t* q, int64_t qrow, int lane, int w) {
     const int h = lane & 15, g = lane >> 4;
     const int64_t base = (qrow * kHeads + h) * kQK;
     scale = 1.f;
+    bx = lx = 0;
     if constexpr (kFp8Mfma) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) b8[c] = *(const i32x8*)(q + base + 128 * c + 32 * g);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) bx[c] = *(const uint64_t*)(q + base + 512 + 32 * c + 8 * g);
+      b8 = *(const i32x8*)(q + base + 128 * w + 32 * g);
+      if (w < 2) bx = *(const uint64_t*)(q + base + 512 + 32 * w + 8 * g);
     } else if constexpr (kHiLo) {
       const uint16_t* qb = (const uint16_t*)q + base;
-      u32x4 raw[4][4];  // chunk c: 32 bf16 = 4 x 16 bytes
-      u32x4 rx[2];
+      u32x4 raw[4];  // main chunk: 32 bf16 = 4 x 16 bytes
+      u32x4 rx = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) raw[c][k] = *(const u32x4*)(qb + 128 * c + 32 * g + 8 * k);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) rx[c] = *(const u32x4*)(qb + 512 + 32 * c + 8 * g);
-      // head-wide max |q| over the 576 dims (144 per lane, 4 lanes per head)
+      for (int k = 0; k < 4; ++k) raw[k] = *(const u32x4*)(qb + 128 * w + 32 * g + 8 * k);
+      if (w < 2) rx = *(const u32x4*)(qb + 512 + 32 * w + 8 * g);
+      // max |q| over this wave's dims of the head (4 lanes per head)
       float amax = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(raw[k][e])), fabsf(bf_hi(raw[k][e]))));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(raw[c][k][e])), fabsf(bf_hi(raw[c][k][e]))));
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(rx[c][e])), fabsf(bf_hi(rx[c][e]))));
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(rx[e])), fabsf(bf_hi(rx[e]))));
       amax = fmaxf(amax, shfl_xor(amax, 16));
       amax = fmaxf(amax, shfl_xor(amax, 32));
       // s = smallest power of two with amax / s <= 448
@@ -494,101 +523,90 @@ struct QOperand {
       ex = amax > 0.f ? std::min(std::max(ex, 1), 253) : 127;
       scale = __builtin_bit_cast(float, (uint32_t)ex << 23);
       const float inv = __builtin_bit_cast(float, (uint32_t)(254 - ex) << 23);
+      u32x4 hw[2], lw[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 hw[2], lw[2];
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            uint32_t hv, lv;
-            split4(raw[c][k][e], raw[c][k][e + 1], inv, hv, lv);
-            hw[k >> 1][2 * (k & 1) + (e >> 1)] = hv;
-            lw[k >> 1][2 * (k & 1) + (e >> 1)] = lv;
-          }
-        b8[c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(hw[0], hw[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        l8[c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lw[0], lw[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        uint32_t h0, l0, h1, l1;
-        split4(rx[c][0], rx[c][1], inv, h0, l0);
-        split4(rx[c][2], rx[c][3], inv, h1, l1);
-        bx[c] = (uint64_t)h0 | ((uint64_t)h1 << 32);
-        lx[c] = (uint64_t)l0 | ((uint64_t)l1 << 32);
-      }
-    } else if constexpr (QF == DT_BF16) {
-#pragma unroll
-      for (int c = 0; c < 18; ++c) b[c] = *(const bf16x8*)(q + 2 * (base + 32 * c + 8 * g));
+        for (int e = 0; e < 4; e += 2) {
+          uint32_t hv, lv;
+          split4(raw[k][e], raw[k][e + 1], inv, hv, lv);
+          hw[k >> 1][2 * (k & 1) + (e >> 1)] = hv;
+          lw[k >> 1][2 * (k & 1) + (e >> 1)] = lv;
+        }
+      b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(hw[0], hw[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      l8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(lw[0], lw[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      uint32_t h0, l0, h1, l1;
+      split4(rx[0], rx[1], inv, h0, l0);
+      split4(rx[2], rx[3], inv, h1, l1);
+      bx = (uint64_t)h0 | ((uint64_t)h1 << 32);
+      lx = (uint64_t)l0 | ((uint64_t)l1 << 32);
     } else {
 #pragma unroll
-      for (int c = 0; c < 18; ++c) b[c] = fp8x8_bf16(*(const u32x2*)(q + base + 32 * c + 8 * g));
+      for (int k = 0; k < kBfChunks; ++k) {
+        const int c = w + 4 * k;
+        if (c < kQK / 32) {
+          if constexpr (QF == DT_BF16)
+            b[k] = *(const bf16x8*)(q + 2 * (base + 32 * c + 8 * g));
+          else
+            b[k] = fp8x8_bf16(*(const u32x2*)(q + base + 32 * c + 8 * g));
+        } else {
+          b[k] = bf16x8{};
+        }
+      }
     }
   }
 
   // Makes the compiler complete the query loads at this point.
   __device__ inline void settle() {
     if constexpr (kByteK) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(b8[c]));
-      asm volatile("" ::"v"(bx[0]), "v"(bx[1]));
-      if constexpr (kHiLo) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(l8[c]));
-        asm volatile("" ::"v"(lx[0]), "v"(lx[1]));
-      }
+      asm volatile("" ::"v"(b8), "v"(bx));
+      if constexpr (kHiLo) asm volatile("" ::"v"(l8), "v"(lx));
     } else {
 #pragma unroll
-      for (int c = 0; c < 18; ++c) asm volatile("" ::"v"(b[c]));
+      for (int k = 0; k < kBfChunks; ++k) asm volatile("" ::"v"(b[k]));
     }
   }
 };
 
-// S^T for the two 16-token blocks of a tile: s[blk][r] = score of token
-// 16 * blk + 4g + r for head lane & 15 (before scaling).  Two independent
-// accumulation chains keep the matrix pipe busy.
+// This wave's partial S^T for the two 16-token blocks of a tile: s[blk][r] =
+// partial score of token 16 * blk + 4g + r for head lane & 15 (before any
+// scaling).  Two independent accumulation chains keep the matrix pipe busy.
 template <int QF, int KF>
-__device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo, int m,
+__device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo, int w, int m,
                                int sdelta, f32x4 s[2]) {
   s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   s[1] = s[0];
   if constexpr (QOperand<QF, KF>::kByteK) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const u32x4 k0 = *(const u32x4*)(st + lo.x[blk][0] + 128 * c);
-        const u32x4 k1 = *(const u32x4*)(st + lo.x[blk][1] + 128 * c);
-        const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
-        // formats 0/0 = fp8 E4M3 for both operands; scale exponents 127 = 2^0
-        s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.b8[c], s[blk], 0, 0, 0, 127, 0, 127);
-        if constexpr (QOperand<QF, KF>::kHiLo)
-          s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.l8[c], s[blk], 0, 0, 0, 127, 0, 127);
-      }
-      // at most two chunks of K operands live at a time
-      if (c & 1) __builtin_amdgcn_sched_barrier(0);
+    for (int blk = 0; blk < 2; ++blk) {
+      const u32x4 k0 = *(const u32x4*)(st + lo.xw[blk][0]);
+      const u32x4 k1 = *(const u32x4*)(st + lo.xw[blk][1]);
+      const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+      // formats 0/0 = fp8 E4M3 for both operands; scale exponents 127 = 2^0
+      s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.b8, s[blk], 0, 0, 0, 127, 0, 127);
+      if constexpr (QOperand<QF, KF>::kHiLo)
+        s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.l8, s[blk], 0, 0, 0, 127, 0, 127);
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    if (w < 2) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        // dims 512 + 32c + 8g + [0, 8) sit where the bf16 path's chunk 16 + c does
-        const uint64_t k = *(const uint64_t*)(st + lo.k[blk][c & 1] + 512);
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.bx[c], s[blk], 0, 0, 0);
+        // rope dims 512 + 32w + 8g + [0, 8) sit where the bf16 path's chunk 16 + w does
+        const uint64_t k = *(const uint64_t*)(st + lo.kr[blk]);
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.bx, s[blk], 0, 0, 0);
         if constexpr (QOperand<QF, KF>::kHiLo)
-          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.lx[c], s[blk], 0, 0, 0);
+          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.lx, s[blk], 0, 0, 0);
       }
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < 18; ++c) {
+    for (int k = 0; k < QOperand<QF, KF>::kBfChunks; ++k) {
+      const int c = w + 4 * k;
+      if (k == QOperand<QF, KF>::kBfChunks - 1 && c >= kQK / 32) break;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 k = load_k8<KF>(st, lo, blk, c, m, sdelta);
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qo.b[c], s[blk], 0, 0, 0);
+        const bf16x8 kk = load_kw<KF>(st, lo, blk, k, w, m, sdelta);
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qo.b[k], s[blk], 0, 0, 0);
       }
-      // keep a few chunks of K in flight, not all 36 operands
-      if (c % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -603,17 +621,35 @@ struct WaveState {
   f32x4 acc[8];
 };
 
+// Partial-score exchange buffer: [wave][block][lane] f32x4.
+constexpr int kXchgBytes = 4 * 2 * 64 * 16;
+
 template <int QF, int KF, bool MASK>
-__device__ inline void process_tile(const uint8_t* st, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo,
-                                    WaveState& ws, int w, int m, int g, int sdelta, int valid, float score_scale) {
+__device__ inline void process_tile(const uint8_t* st, f32x4* xchg, const QOperand<QF, KF>& qo,
+                                    const LaneOffs<KF>& lo, WaveState& ws, int w, int m, int g, int sdelta, int valid,
+                                    float score_scale) {
+  const int lane = threadIdx.x & 63;
+  {
+    f32x4 part[2];
+    qk_tile<QF, KF>(st, qo, lo, w, m, sdelta, part);
+    xchg[(2 * w + 0) * 64 + lane] = part[0] * qo.scale;
+    xchg[(2 * w + 1) * 64 + lane] = part[1] * qo.scale;
+  }
+  lds_barrier();  // every wave's partial scores are in LDS
   f32x4 s[2];
-  qk_tile<QF, KF>(st, qo, lo, m, sdelta, s);
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    // same summation order in every wave, so all four see identical scores
+    s[blk] = xchg[(0 + blk) * 64 + lane];
+    s[blk] += xchg[(2 + blk) * 64 + lane];
+    s[blk] += xchg[(4 + blk) * 64 + lane];
+    s[blk] += xchg[(6 + blk) * 64 + lane];
+  }
   float t[8];
   float mx = -INFINITY;
-  const float sc = score_scale * qo.scale;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    t[k] = s[k >> 2][k & 3] * sc;
+    t[k] = s[k >> 2][k & 3] * score_scale;
     if (MASK && pv_row(g, k) >= valid) t[k] = -INFINITY;
     mx = fmaxf(mx, t[k]);
   }
@@ -651,7 +687,7 @@ __device__ inline void process_tile(const uint8_t* st, const QOperand<QF, KF>& q
 }
 
 template <int QF, int KF>
-__device__ void split_piece(const SplitParams& p, uint8_t* ring, int64_t qrow, int64_t r0, int n, int32_t slot,
+__device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, int64_t qrow, int64_t r0, int n, int32_t slot,
                             float score_scale, float out_scale) {
   using G = Geom<KF>;
   constexpr int NS = G::kStages;
@@ -697,10 +733,10 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, int64_t qrow, i
   };
 
   LaneOffs<KF> lo;
-  lo.init(m, g);
+  lo.init(m, g, w);
 
   QOperand<QF, KF> qop;
-  qop.load(p.q, qrow, lane);
+  qop.load(p.q, qrow, lane, w);
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
   // Make the compiler complete the query loads here (its wait also covers the
@@ -723,9 +759,9 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, int64_t qrow, i
     const int valid = std::min(kTile, n - i * kTile);
     const int sdelta = (KF == DT_MXFP4) ? (int)(((r0 + (int64_t)i * kTile) * kScaleRow) & 15) : 0;
     if (valid < kTile)
-      process_tile<QF, KF, true>(st, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
+      process_tile<QF, KF, true>(st, xchg, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
     else
-      process_tile<QF, KF, false>(st, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
+      process_tile<QF, KF, false>(st, xchg, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
   }
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
@@ -759,7 +795,8 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
     SplitParams p) {
   using G = Geom<KF>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[G::kLdsBytes];
-  __shared__ int counts[2];
+  __shared__ f32x4 xchg[kXchgBytes / 16];
+  int* counts = (int*)xchg;  // the sequence search runs before any exchange
 
   const int tid = threadIdx.x;
   const int32_t gi = blockIdx.x;
@@ -801,7 +838,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
     const int64_t qrow = std::min(std::max(uniform(p.qo_indptr[b]), 0), p.total_q - 1);
-    split_piece<QF, KF>(p, ring, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale);
+    split_piece<QF, KF>(p, ring, xchg, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale);
     lds_barrier();  // the next piece refills the ring
   }
 }
@@ -936,9 +973,9 @@ int tile_stages(int kv_dtype) {
 
 int lds_bytes_for(int kv_dtype) {
   switch (kv_dtype) {
-    case DT_BF16: return Geom<DT_BF16>::kLdsBytes;
-    case DT_FP8: return Geom<DT_FP8>::kLdsBytes;
-    default: return Geom<DT_MXFP4>::kLdsBytes;
+    case DT_BF16: return Geom<DT_BF16>::kLdsBytes + kXchgBytes;
+    case DT_FP8: return Geom<DT_FP8>::kLdsBytes + kXchgBytes;
+    default: return Geom<DT_MXFP4>::kLdsBytes + kXchgBytes;
   }
 }
 
