@@ -492,21 +492,65 @@ struct QOperand {
   uint64_t lx;
   float scale;          // factor of this wave's partial scores (s for the split form, else 1)
 
-  __device__ inline void load(const uint8_t* q, int64_t qrow, int lane, int w) {
+  // Raw query words as loaded (hi/lo form: 32 + 8 bf16; bf16 form with fp8 q: codes).
+  u32x4 raw[4];
+  u32x4 rx;
+  u32x2 r8[kBfChunks];
+
+  // Issues this wave's query loads (phase 1 of 3).
+  __device__ inline void fetch(const uint8_t* q, int64_t qrow, int lane, int w) {
     const int h = lane & 15, g = lane >> 4;
     const int64_t base = (qrow * kHeads + h) * kQK;
-    scale = 1.f;
     bx = lx = 0;
+    rx = u32x4{0u, 0u, 0u, 0u};
     if constexpr (kFp8Mfma) {
       b8 = *(const i32x8*)(q + base + 128 * w + 32 * g);
       if (w < 2) bx = *(const uint64_t*)(q + base + 512 + 32 * w + 8 * g);
     } else if constexpr (kHiLo) {
       const uint16_t* qb = (const uint16_t*)q + base;
-      u32x4 raw[4];  // main chunk: 32 bf16 = 4 x 16 bytes
-      u32x4 rx = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int k = 0; k < 4; ++k) raw[k] = *(const u32x4*)(qb + 128 * w + 32 * g + 8 * k);
       if (w < 2) rx = *(const u32x4*)(qb + 512 + 32 * w + 8 * g);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kBfChunks; ++k) {
+        const int c = w + 4 * k;
+        if (c < kQK / 32) {
+          if constexpr (QF == DT_BF16)
+            b[k] = *(const bf16x8*)(q + 2 * (base + 32 * c + 8 * g));
+          else
+            r8[k] = *(const u32x2*)(q + base + 32 * c + 8 * g);
+        } else {
+          b[k] = bf16x8{};
+          r8[k] = u32x2{0u, 0u};
+        }
+      }
+    }
+  }
+
+  // Makes the compiler complete the query loads here (phase 2), before any
+  // KV DMA is issued: the compiler's wait for them would otherwise also wait
+  // for every DMA issued in between.
+  __device__ inline void arrive() {
+    if constexpr (kFp8Mfma) {
+      asm volatile("" ::"v"(b8), "v"(bx));
+    } else if constexpr (kHiLo) {
+      asm volatile("" ::"v"(raw[0]), "v"(raw[1]), "v"(raw[2]), "v"(raw[3]), "v"(rx));
+    } else if constexpr (QF == DT_BF16) {
+#pragma unroll
+      for (int k = 0; k < kBfChunks; ++k) asm volatile("" ::"v"(b[k]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < kBfChunks; ++k) asm volatile("" ::"v"(r8[k]));
+    }
+  }
+
+  // Builds the operand from the raw words (phase 3).  The empty asm keeps this
+  // arithmetic after the DMA issued between arrive() and here.
+  __device__ inline void prepare() {
+    scale = 1.f;
+    if constexpr (kHiLo) {
+      asm volatile("" : "+v"(raw[0]), "+v"(raw[1]), "+v"(raw[2]), "+v"(raw[3]), "+v"(rx));
       // max |q| over this wave's dims of the head (4 lanes per head)
       float amax = 0.f;
 #pragma unroll
@@ -540,23 +584,17 @@ struct QOperand {
       split4(rx[2], rx[3], inv, h1, l1);
       bx = (uint64_t)h0 | ((uint64_t)h1 << 32);
       lx = (uint64_t)l0 | ((uint64_t)l1 << 32);
-    } else {
+    } else if constexpr (!kFp8Mfma && QF == DT_FP8) {
 #pragma unroll
       for (int k = 0; k < kBfChunks; ++k) {
-        const int c = w + 4 * k;
-        if (c < kQK / 32) {
-          if constexpr (QF == DT_BF16)
-            b[k] = *(const bf16x8*)(q + 2 * (base + 32 * c + 8 * g));
-          else
-            b[k] = fp8x8_bf16(*(const u32x2*)(q + base + 32 * c + 8 * g));
-        } else {
-          b[k] = bf16x8{};
-        }
+        asm volatile("" : "+v"(r8[k]));
+        b[k] = fp8x8_bf16(r8[k]);
       }
     }
   }
 
-  // Makes the compiler complete the query loads at this point.
+  // Keeps the finished operand in registers from here on (the compiler would
+  // otherwise be free to re-derive parts of it inside the tile loop).
   __device__ inline void settle() {
     if constexpr (kByteK) {
       asm volatile("" ::"v"(b8), "v"(bx));
@@ -736,12 +774,11 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, in
   lo.init(m, g, w);
 
   QOperand<QF, KF> qop;
-  qop.load(p.q, qrow, lane, w);
+  qop.fetch(p.q, qrow, lane, w);
+  qop.arrive();
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
-  // Make the compiler complete the query loads here (its wait also covers the
-  // prologue DMA issued after them); otherwise it would place those waits in
-  // the tile loop, where they would drain the whole DMA ring every tile.
+  qop.prepare();
   qop.settle();
 
   WaveState ws;
@@ -832,12 +869,14 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
   const float out_scale = ks;
 
   for (int b = b_first; b < b_end; ++b) {
-    const int64_t s = uniform(p.kv_indptr[b]);
-    const int64_t e = uniform(p.kv_indptr[b + 1]);
+    // the three loads are independent; issue them together
+    const int32_t s_raw = p.kv_indptr[b], e_raw = p.kv_indptr[b + 1], q_raw = p.qo_indptr[b];
+    const int64_t s = uniform(s_raw);
+    const int64_t e = uniform(e_raw);
+    const int64_t qrow = std::min(std::max(uniform(q_raw), 0), p.total_q - 1);
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
-    const int64_t qrow = std::min(std::max(uniform(p.qo_indptr[b]), 0), p.total_q - 1);
     split_piece<QF, KF>(p, ring, xchg, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale);
     lds_barrier();  // the next piece refills the ring
   }
@@ -857,13 +896,20 @@ struct MergeParams {
   int32_t num_wgs;
 };
 
-// One workgroup of 128 threads per (sequence, head); thread t owns columns 4t..4t+3.
+// One workgroup of 128 threads per (sequence, head); thread t owns columns
+// 4t..4t+3.  The log-sum-exps and partial outputs of up to kMergeBatch slots
+// are loaded together (none depends on another), then combined with a running
+// maximum, so a sequence of up to kMergeBatch pieces costs one round trip to
+// memory after the index loads.
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p) {
   const int b = blockIdx.x >> 4, h = blockIdx.x & 15;
   const int t = threadIdx.x;
-  const int64_t s = std::max<int64_t>(p.kv_indptr[b], 0);
-  const int64_t e = std::min<int64_t>(p.kv_indptr[b + 1], p.total_kv);
-  const int64_t qrow = std::min(std::max(p.qo_indptr[b], 0), p.total_q - 1);
+  const int32_t s_raw = p.kv_indptr[b], e_raw = p.kv_indptr[b + 1], q_raw = p.qo_indptr[b];
+  const int64_t s = std::max<int64_t>(s_raw, 0);
+  const int64_t e = std::min<int64_t>(e_raw, p.total_kv);
+  const int64_t qrow = std::min(std::max(q_raw, 0), p.total_q - 1);
   uint16_t* o = p.out + (qrow * kHeads + h) * kV + 4 * t;
   if (e <= s) {  // no KV rows: the softmax is empty, the output is zero
     *(uint2*)o = make_uint2(0u, 0u);
@@ -872,17 +918,35 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p) {
   const int32_t g0 = (int32_t)std::min<int64_t>(s / p.rows_per_wg, p.num_wgs - 1);
   const int32_t g1 = (int32_t)std::min<int64_t>((e - 1) / p.rows_per_wg, p.num_wgs - 1);
   if (g0 == g1) return;  // written by stage 1
-  float mx = -INFINITY;
-  for (int32_t g = g0; g <= g1; ++g) mx = fmaxf(mx, p.part_lse[(int64_t)merge_slot(g, g0) * kHeads + h]);
-  float wsum = 0.f;
+  float m_run = -INFINITY, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t g = g0; g <= g1; ++g) {
-    const int64_t slot = merge_slot(g, g0);
-    const float lse = p.part_lse[slot * kHeads + h];
-    const float wgt = (lse == -INFINITY) ? 0.f : __expf(lse - mx);
-    wsum += wgt;
-    const f32x4 v = *(const f32x4*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
-    acc += wgt * v;
+  for (int32_t base = g0; base <= g1; base += kMergeBatch) {
+    float lse[kMergeBatch];
+    f32x4 v[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      lse[k] = -INFINITY;
+      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (base + k <= g1) {
+        const int64_t slot = merge_slot(base + k, g0);
+        lse[k] = p.part_lse[slot * kHeads + h];
+        v[k] = *(const f32x4*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
+      }
+    }
+    float mx = m_run;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) mx = fmaxf(mx, lse[k]);
+    if (mx == -INFINITY) continue;  // only empty slices so far
+    const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - mx);
+    wsum *= alpha;
+    acc *= alpha;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wgt = (lse[k] == -INFINITY) ? 0.f : __expf(lse[k] - mx);
+      wsum += wgt;
+      acc += wgt * v[k];
+    }
+    m_run = mx;
   }
   const float inv = 1.f / wsum;
   *(uint2*)o = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
