@@ -61,7 +61,7 @@ typedef struct mla_problem {
   int32_t v_dim;      /* value width; must be 512 (first columns of the KV row) */
   int32_t q_dtype;    /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3FN */
   int32_t kv_dtype;   /* any mla_dtype; fp8 q requires fp8 KV */
-  float sm_scale;     /* softmax scale, 1/sqrt(576) for DeepSeek-R1 */
+  float sm_scale;     /* softmax scale, 1/sqrt(576) for DeepSeek-R1; finite and > 0 */
   int32_t num_cus;    /* compute units to plan for; 0 = ask the current HIP device */
 } mla_problem;
 
@@ -111,9 +111,9 @@ mla_status mla_decode_plan(const mla_problem* problem, const mla_plan_options* o
  * the plan needs it).  No allocation, no host<->device copy, no synchronisation.
  * All device pointers must be 16-byte aligned.
  *   q          device, [total_q][16][576]: bf16, or fp8 E4M3FN codes when q_dtype is fp8.
- *   q_scale    device fp32[1] (fp8 q: q = code * q_scale); ignored for bf16 q (may be NULL).
+ *   q_scale    device fp32[1] (fp8 q: q = code * q_scale, q_scale >= 0); ignored for bf16 q (may be NULL).
  *   kv         device, [total_kv][576] bf16 | [total_kv][576] fp8 codes | [total_kv][288] MXFP4 bytes.
- *   kv_scale   fp8 KV: device fp32[1] (kv = code * kv_scale).
+ *   kv_scale   fp8 KV: device fp32[1] (kv = code * kv_scale, kv_scale >= 0).
  *              MXFP4 KV: device uint8 [total_kv][18] E8M0 bytes, one per 32 columns,
  *              read in 16-byte units: the allocation must be readable up to the next
  *              multiple of 16 bytes past total_kv*18.

@@ -546,12 +546,15 @@ struct QOperand {
   }
 
   // Builds the operand from the raw words (phase 3).  The empty asm keeps this
-  // arithmetic after the DMA issued between arrive() and here.
-  __device__ inline void prepare() {
+  // arithmetic after the DMA issued between arrive() and here.  For the split
+  // form the four waves agree on one scale per head (through `amax_lds`, 64
+  // floats of LDS, with a workgroup barrier), so their partial scores add
+  // without rescaling.  Every wave of the workgroup must call it.
+  __device__ inline void prepare(float* amax_lds, int w, int lane) {
     scale = 1.f;
     if constexpr (kHiLo) {
       asm volatile("" : "+v"(raw[0]), "+v"(raw[1]), "+v"(raw[2]), "+v"(raw[3]), "+v"(rx));
-      // max |q| over this wave's dims of the head (4 lanes per head)
+      // max |q| over this wave's dims of the head (4 lanes per head), then over the waves
       float amax = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -561,6 +564,10 @@ struct QOperand {
       for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(rx[e])), fabsf(bf_hi(rx[e]))));
       amax = fmaxf(amax, shfl_xor(amax, 16));
       amax = fmaxf(amax, shfl_xor(amax, 32));
+      if (lane < 16) amax_lds[16 * w + lane] = amax;
+      lds_barrier();
+      const int h = lane & 15;
+      amax = fmaxf(fmaxf(amax_lds[h], amax_lds[16 + h]), fmaxf(amax_lds[32 + h], amax_lds[48 + h]));
       // s = smallest power of two with amax / s <= 448
       const uint32_t tb = __builtin_bit_cast(uint32_t, amax * (1.0f / 448.0f));
       int ex = (int)((tb >> 23) & 255u) + ((tb & 0x7fffffu) ? 1 : 0);
@@ -670,8 +677,8 @@ __device__ inline void process_tile(const uint8_t* st, f32x4* xchg, const QOpera
   {
     f32x4 part[2];
     qk_tile<QF, KF>(st, qo, lo, w, m, sdelta, part);
-    xchg[(2 * w + 0) * 64 + lane] = part[0] * qo.scale;
-    xchg[(2 * w + 1) * 64 + lane] = part[1] * qo.scale;
+    xchg[(2 * w + 0) * 64 + lane] = part[0];
+    xchg[(2 * w + 1) * 64 + lane] = part[1];
   }
   lds_barrier();  // every wave's partial scores are in LDS
   f32x4 s[2];
@@ -683,14 +690,17 @@ __device__ inline void process_tile(const uint8_t* st, f32x4* xchg, const QOpera
     s[blk] += xchg[(4 + blk) * 64 + lane];
     s[blk] += xchg[(6 + blk) * 64 + lane];
   }
-  float t[8];
+  // raw sums; the base-2 score is sv * c with c > 0 (so max(sv) * c is the max score)
+  const float c = score_scale * qo.scale;
+  float sv[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    t[k] = s[k >> 2][k & 3] * score_scale;
-    if (MASK && pv_row(g, k) >= valid) t[k] = -INFINITY;
-    mx = fmaxf(mx, t[k]);
+    sv[k] = s[k >> 2][k & 3];
+    if (MASK && pv_row(g, k) >= valid) sv[k] = -INFINITY;
+    mx = fmaxf(mx, sv[k]);
   }
+  mx *= c;
   // The reference max m_run is raised (to the exact head-wide maximum) and the
   // accumulators rescaled only when a score exceeds it by more than
   // kRescaleSlack; otherwise p = 2^(t - m_run) <= 2^kRescaleSlack, which bf16
@@ -711,8 +721,8 @@ __device__ inline void process_tile(const uint8_t* st, f32x4* xchg, const QOpera
   float ps = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float p0 = __builtin_amdgcn_exp2f(t[2 * k] - ws.m_run);
-    const float p1 = __builtin_amdgcn_exp2f(t[2 * k + 1] - ws.m_run);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * k], c, -ws.m_run));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * k + 1], c, -ws.m_run));
     ps += p0 + p1;
     pk[k] = pack_bf16x2(p0, p1);
   }
@@ -778,7 +788,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, in
   qop.arrive();
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
-  qop.prepare();
+  qop.prepare((float*)xchg + 256, w, lane);  // clear of the sequence counts at the start of xchg
   qop.settle();
 
   WaveState ws;
@@ -788,17 +798,27 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, in
   for (int j = 0; j < 8; ++j) ws.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int my_chunks = G::chunks_of_wave(w);
-  for (int i = 0; i < ntiles; ++i) {
+  // tile i is complete in LDS and every wave is done with tile i - 1
+  auto advance = [&](int i) {
     wait_tiles_behind<G::kMaxChunksPerWave>(my_chunks, std::min(NS - 2, ntiles - 1 - i));
-    lds_barrier();  // tile i is complete in LDS; both waves are done with tile i - 1
+    lds_barrier();
     if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
-    const uint8_t* st = ring + (i % NS) * G::kStageBytes;
-    const int valid = std::min(kTile, n - i * kTile);
-    const int sdelta = (KF == DT_MXFP4) ? (int)(((r0 + (int64_t)i * kTile) * kScaleRow) & 15) : 0;
-    if (valid < kTile)
-      process_tile<QF, KF, true>(st, xchg, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
-    else
-      process_tile<QF, KF, false>(st, xchg, qop, lo, ws, w, m, g, sdelta, valid, score_scale);
+  };
+  auto sdelta_of = [&](int i) {
+    return (KF == DT_MXFP4) ? (int)(((r0 + (int64_t)i * kTile) * kScaleRow) & 15) : 0;
+  };
+  // full tiles in the loop (one code path, so the accumulators stay in place);
+  // a partial last tile after it
+  const int nfull = n / kTile;
+  for (int i = 0; i < nfull; ++i) {
+    advance(i);
+    process_tile<QF, KF, false>(ring + (i % NS) * G::kStageBytes, xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile,
+                                score_scale);
+  }
+  if (nfull < ntiles) {
+    advance(nfull);
+    process_tile<QF, KF, true>(ring + (nfull % NS) * G::kStageBytes, xchg, qop, lo, ws, w, m, g, sdelta_of(nfull),
+                               n - nfull * kTile, score_scale);
   }
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
@@ -1081,7 +1101,10 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
                            mla_plan** plan_out, size_t* workspace_bytes) {
   if (plan_out) *plan_out = nullptr;
   if (!pr || !plan_out) return MLA_ERR_INVALID_ARG;
-  if (pr->batch_size < 1 || pr->total_kv < 0 || pr->total_kv > INT32_MAX || !(pr->sm_scale == pr->sm_scale))
+  // sm_scale must be finite and positive (the kernel takes the maximum score as
+  // sm_scale times the maximum dot product)
+  if (pr->batch_size < 1 || pr->total_kv < 0 || pr->total_kv > INT32_MAX || !(pr->sm_scale > 0.f) ||
+      !(pr->sm_scale < INFINITY))
     return MLA_ERR_INVALID_ARG;
   if (pr->num_heads != kHeads || pr->qk_dim != kQK || pr->v_dim != kV) return MLA_ERR_UNSUPPORTED;
   if (pr->total_q != pr->batch_size) return MLA_ERR_UNSUPPORTED;  // one query token per sequence

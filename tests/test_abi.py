@@ -160,6 +160,9 @@ def test_plan_argument_errors():
     assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_UNSUPPORTED
     prob = mla.make_problem(0, 100, num_cus=256)
     assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG
+    for bad in (0.0, -1.0 / 24, float("nan"), float("inf")):
+        prob = mla.make_problem(4, 100, num_cus=256, sm_scale=bad)
+        assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG, bad
     prob = mla.make_problem(3, 100, num_cus=256)
     assert _status(mla.mla_decode_plan, prob, None, np.array([0, 50, 40, 100], np.int32)) == mla.MLA_ERR_INVALID_ARG
     assert _status(mla.mla_decode_plan, prob, None, np.array([0, 50, 60, 101], np.int32)) == mla.MLA_ERR_INVALID_ARG
