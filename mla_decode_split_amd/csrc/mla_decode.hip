@@ -734,9 +734,28 @@ __device__ inline void process_tile(const uint8_t* st, f32x4* xchg, const QOpera
   for (int j = 0; j < 8; ++j) ws.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, ws.acc[j], 0, 0, 0);
 }
 
+// Two workgroups share each CU, and the SIMD arbiter favours older waves, so
+// with equal priorities the workgroup dispatched second falls behind and the
+// kernel waits for it.  Each wave's priority instead follows how much of its
+// workgroup's row range is left (3 above one half, 2 above a quarter, 1 above
+// an eighth, else 0): whichever workgroup lags is favoured until it catches up.
+__device__ inline int range_priority(int64_t remaining, int32_t range_rows) {
+  const int64_t r = remaining * 8;
+  return r > 4 * (int64_t)range_rows ? 3 : r > 2 * (int64_t)range_rows ? 2 : r > range_rows ? 1 : 0;
+}
+
+__device__ inline void set_priority(int prio) {
+  switch (prio) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 template <int QF, int KF>
 __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, int64_t qrow, int64_t r0, int n, int32_t slot,
-                            float score_scale, float out_scale) {
+                            float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
   using G = Geom<KF>;
   constexpr int NS = G::kStages;
   const int lane = threadIdx.x & 63;
@@ -810,7 +829,13 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, in
   // full tiles in the loop (one code path, so the accumulators stay in place);
   // a partial last tile after it
   const int nfull = n / kTile;
+  int prio = -1;
   for (int i = 0; i < nfull; ++i) {
+    const int want = range_priority(wg_hi - (r0 + (int64_t)i * kTile), wg_rows);
+    if (want != prio) {
+      prio = want;
+      set_priority(prio);
+    }
     advance(i);
     process_tile<QF, KF, false>(ring + (i % NS) * G::kStageBytes, xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile,
                                 score_scale);
@@ -897,7 +922,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
-    split_piece<QF, KF>(p, ring, xchg, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale);
+    split_piece<QF, KF>(p, ring, xchg, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
     lds_barrier();  // the next piece refills the ring
   }
 }
