@@ -348,8 +348,12 @@ struct LaneOffs {
         kr[blk] = 0;
         kb[blk] = row * R + 16 * (g ^ f) + 64 * w;
       } else {
-        kr[blk] = 0;
-        kb[blk] = row * R + 16 * (par ^ f) + 4 * g + 32 * (w >> 1);
+        // main chunk w: the 32 E2M1 codes of dims 128w + 32g + [0, 32) are unit 4w + g;
+        // rope (waves 0, 1): dims 512 + 32w + 8g + [0, 8) are unit 16 + w, byte 4g
+        xw[blk][0] = row * R + 16 * ((4 * w + g) ^ f);
+        xw[blk][1] = 0;
+        kr[blk] = row * R + 16 * ((16 + (w & 1)) ^ f) + 4 * g;
+        kb[blk] = 0;
       }
     }
 #pragma unroll
@@ -371,17 +375,11 @@ struct LaneOffs {
 };
 
 // K operand of the bf16 path: key dims [32c + 8g, 32c + 8g + 8) of token
-// block blk, as bf16, for this wave's chunk c = w + 4k.
+// block blk for this wave's chunk c = w + 4k.
 template <int KF>
-__device__ inline bf16x8 load_kw(const uint8_t* st, const LaneOffs<KF>& lo, int blk, int k, int w, int m, int sdelta) {
-  if constexpr (KF == DT_BF16) {
-    return *(const bf16x8*)(st + lo.kb[blk] + 256 * k);
-  } else {
-    static_assert(KF == DT_MXFP4, "fp8 keys use the byte path");
-    const uint32_t word = *(const uint32_t*)(st + lo.kb[blk] + 64 * k);
-    const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + w + 4 * k];
-    return fp4x8_bf16(word, e8m0_f32(e));
-  }
+__device__ inline bf16x8 load_kw(const uint8_t* st, const LaneOffs<KF>& lo, int blk, int k) {
+  static_assert(KF == DT_BF16, "fp8 and E2M1 keys use the matrix unit's own formats");
+  return *(const bf16x8*)(st + lo.kb[blk] + 256 * k);
 }
 
 // V^T operands (A of O^T = V^T P^T) for value columns 128q + 8m + j (j = 0..7):
@@ -466,31 +464,37 @@ struct SplitParams {
 // waves of a workgroup split the 576 dims (each computes a partial S^T over
 // its share for all tokens of the tile; the partials are summed through LDS),
 // so every product is computed once.  Lane (head = lane & 15, group = lane >> 4)
-// holds, laid out like the K operand:
-//   byte-K forms: dims 128w + 32g + [0, 32) (one 16x16x128 chunk) and, for
-//                 waves 0 and 1, rope dims 512 + 32w + 8g + [0, 8);
-//   bf16 form   : dims 32c + 8g + [0, 8) of chunks c = w + 4k, k < 5, c < 18.
-// The three operand kinds:
-//   fp8 q, fp8 KV  : the fp8 codes, multiplied by fp8 K on the fp8 matrix unit;
-//   bf16 q, fp8 KV : q / s split into two fp8 terms hi + lo with a power-of-two
-//                    s per (wave, head) (hi = E4M3(q / s), lo = E4M3(q / s - hi)).
+// holds:
+//   fp8 keys      : dims 128w + 32g + [0, 32) (one 16x16x128 chunk, laid out like
+//                   K) and, for waves 0 and 1, rope dims 512 + 32w + 8g + [0, 8);
+//   E2M1 keys     : dims 128w + 16g + [0, 16) and 128w + 64 + 16g + [0, 16) - the
+//                   16x16x128 instruction pairs these with the A lane group that
+//                   holds key dims 128w + 32g' + [0, 32) (one E8M0 block per lane,
+//                   which is what the per-lane A scale applies to) - and, for
+//                   waves 0 and 1, the bf16 rope dims 512 + 32w + 8g + [0, 8);
+//   bf16 keys     : dims 32c + 8g + [0, 8) of chunks c = w + 4k, k < 5, c < 18.
+// The operand kinds:
+//   fp8 q with fp8 / E2M1 keys : the fp8 codes, on the matrix unit's own formats;
+//   bf16 q with fp8 / E2M1 keys: q / s split into two fp8 terms hi + lo with one
+//                    power-of-two s per head (hi = E4M3(q / s), lo = E4M3(q / s - hi)).
 //                    A bf16 value has 8 significant bits and hi, lo carry 4 each,
 //                    so the split is exact except for elements far below the
-//                    maximum the scale is chosen for; K then feeds the fp8 matrix
-//                    unit unconverted;
-//   otherwise      : bf16 (fp8 q widened exactly), multiplied by K widened to bf16.
+//                    head's maximum; keys feed the matrix unit unconverted;
+//   bf16 keys      : bf16 (fp8 q widened exactly).
 template <int QF, int KF>
 struct QOperand {
-  static constexpr bool kFp8Mfma = (QF == DT_FP8 && KF == DT_FP8);
-  static constexpr bool kHiLo = (QF == DT_BF16 && KF == DT_FP8);
-  static constexpr bool kByteK = kFp8Mfma || kHiLo;  // K used as raw fp8 bytes
+  static constexpr bool kByteK = (KF == DT_FP8);    // K fed as raw fp8 bytes
+  static constexpr bool kFp4K = (KF == DT_MXFP4);   // K fed as raw E2M1 codes with their E8M0 scales
+  static constexpr bool kFp8Codes = (QF == DT_FP8 && (kByteK || kFp4K));  // q's fp8 codes as the B operand
+  static constexpr bool kHiLo = (QF == DT_BF16 && (kByteK || kFp4K));     // bf16 q split into two fp8 terms
   static constexpr int kBfChunks = 5;
-  bf16x8 b[kBfChunks];  // bf16 form
+  bf16x8 b[kBfChunks];  // bf16 form (bf16 KV)
   i32x8 b8;             // fp8 forms (hi term): main chunk
-  uint64_t bx;          //                      rope chunk (waves 0, 1)
+  uint64_t bx;          //                      rope chunk (waves 0, 1), fp8 KV
   i32x8 l8;             // split form, lo term
   uint64_t lx;
-  float scale;          // factor of this wave's partial scores (s for the split form, else 1)
+  bf16x8 br;            // rope chunk (waves 0, 1) of the E2M1 path, bf16 (divided by the split scale)
+  float scale;          // factor of the scores (s for the split form, else 1)
 
   // Raw query words as loaded (hi/lo form: 32 + 8 bf16; bf16 form with fp8 q: codes).
   u32x4 raw[4];
@@ -503,13 +507,29 @@ struct QOperand {
     const int64_t base = (qrow * kHeads + h) * kQK;
     bx = lx = 0;
     rx = u32x4{0u, 0u, 0u, 0u};
-    if constexpr (kFp8Mfma) {
-      b8 = *(const i32x8*)(q + base + 128 * w + 32 * g);
-      if (w < 2) bx = *(const uint64_t*)(q + base + 512 + 32 * w + 8 * g);
+    r8[0] = u32x2{0u, 0u};
+    // For E2M1 keys the matrix unit pairs the 32 K values of B lane group g with
+    // A values that, given A lane group g' = dims 32g' + [0, 32) of the chunk (one
+    // E8M0 block per lane, as the per-lane A scale requires), are dims
+    // 16g + [0, 16) and 64 + 16g + [0, 16); for fp8 keys B lane group g holds
+    // dims 32g + [0, 32).
+    const int m0 = kFp4K ? 128 * w + 16 * g : 128 * w + 32 * g;  // first 16 dims of this lane's B part
+    const int m1 = kFp4K ? m0 + 64 : m0 + 16;                     // second 16
+    if constexpr (kFp8Codes) {
+      b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(*(const u32x4*)(q + base + m0),
+                                                             *(const u32x4*)(q + base + m1), 0, 1, 2, 3, 4, 5, 6, 7));
+      if (w < 2) {
+        if constexpr (kByteK)
+          bx = *(const uint64_t*)(q + base + 512 + 32 * w + 8 * g);
+        else
+          r8[0] = *(const u32x2*)(q + base + 512 + 32 * w + 8 * g);
+      }
     } else if constexpr (kHiLo) {
       const uint16_t* qb = (const uint16_t*)q + base;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) raw[k] = *(const u32x4*)(qb + 128 * w + 32 * g + 8 * k);
+      raw[0] = *(const u32x4*)(qb + m0);
+      raw[1] = *(const u32x4*)(qb + m0 + 8);
+      raw[2] = *(const u32x4*)(qb + m1);
+      raw[3] = *(const u32x4*)(qb + m1 + 8);
       if (w < 2) rx = *(const u32x4*)(qb + 512 + 32 * w + 8 * g);
     } else {
 #pragma unroll
@@ -532,8 +552,8 @@ struct QOperand {
   // KV DMA is issued: the compiler's wait for them would otherwise also wait
   // for every DMA issued in between.
   __device__ inline void arrive() {
-    if constexpr (kFp8Mfma) {
-      asm volatile("" ::"v"(b8), "v"(bx));
+    if constexpr (kFp8Codes) {
+      asm volatile("" ::"v"(b8), "v"(bx), "v"(r8[0]));
     } else if constexpr (kHiLo) {
       asm volatile("" ::"v"(raw[0]), "v"(raw[1]), "v"(raw[2]), "v"(raw[3]), "v"(rx));
     } else if constexpr (QF == DT_BF16) {
@@ -586,12 +606,23 @@ struct QOperand {
         }
       b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(hw[0], hw[1], 0, 1, 2, 3, 4, 5, 6, 7));
       l8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(lw[0], lw[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      uint32_t h0, l0, h1, l1;
-      split4(rx[0], rx[1], inv, h0, l0);
-      split4(rx[2], rx[3], inv, h1, l1);
-      bx = (uint64_t)h0 | ((uint64_t)h1 << 32);
-      lx = (uint64_t)l0 | ((uint64_t)l1 << 32);
-    } else if constexpr (!kFp8Mfma && QF == DT_FP8) {
+      if constexpr (kByteK) {
+        uint32_t h0, l0, h1, l1;
+        split4(rx[0], rx[1], inv, h0, l0);
+        split4(rx[2], rx[3], inv, h1, l1);
+        bx = (uint64_t)h0 | ((uint64_t)h1 << 32);
+        lx = (uint64_t)l0 | ((uint64_t)l1 << 32);
+      } else {
+        // rope stays bf16; dividing by the power of two s is exact
+        u32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(bf_lo(rx[e]) * inv, bf_hi(rx[e]) * inv);
+        br = __builtin_bit_cast(bf16x8, r);
+      }
+    } else if constexpr (kFp8Codes && kFp4K) {
+      asm volatile("" : "+v"(r8[0]));
+      br = fp8x8_bf16(r8[0]);
+    } else if constexpr (!kFp8Codes && QF == DT_FP8) {
 #pragma unroll
       for (int k = 0; k < kBfChunks; ++k) {
         asm volatile("" : "+v"(r8[k]));
@@ -603,9 +634,10 @@ struct QOperand {
   // Keeps the finished operand in registers from here on (the compiler would
   // otherwise be free to re-derive parts of it inside the tile loop).
   __device__ inline void settle() {
-    if constexpr (kByteK) {
+    if constexpr (kByteK || kFp4K) {
       asm volatile("" ::"v"(b8), "v"(bx));
       if constexpr (kHiLo) asm volatile("" ::"v"(l8), "v"(lx));
+      if constexpr (kFp4K) asm volatile("" ::"v"(br));
     } else {
 #pragma unroll
       for (int k = 0; k < kBfChunks; ++k) asm volatile("" ::"v"(b[k]));
@@ -642,6 +674,29 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, co
           s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.lx, s[blk], 0, 0, 0);
       }
     }
+  } else if constexpr (QOperand<QF, KF>::kFp4K) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      // A lane group g: the 32 E2M1 codes of dims 128w + 32g + [0, 32), one E8M0
+      // block, in natural order (the upper half of the operand is unused for
+      // 4-bit data); the query operand holds the dims they pair with
+      const u32x4 k4 = *(const u32x4*)(st + lo.xw[blk][0]);
+      const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k4, u32x4{0u, 0u, 0u, 0u}, 0, 1, 2, 3, 4, 5, 6, 7));
+      const int e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + 4 * w + (threadIdx.x & 63) / 16];
+      // formats: A = 4 (E2M1), B = 0 (fp8 E4M3); B scale exponent 127 = 2^0
+      s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.b8, s[blk], 4, 0, 0, e, 0, 127);
+      if constexpr (QOperand<QF, KF>::kHiLo)
+        s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.l8, s[blk], 4, 0, 0, e, 0, 127);
+    }
+    if (w < 2) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        // rope dims 512 + 32w + 8g + [0, 8), widened to bf16 with their block scale
+        const uint32_t word = *(const uint32_t*)(st + lo.kr[blk]);
+        const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + 16 + w];
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16(word, e8m0_f32(e)), qo.br, s[blk], 0, 0, 0);
+      }
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < QOperand<QF, KF>::kBfChunks; ++k) {
@@ -649,7 +704,7 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, co
       if (k == QOperand<QF, KF>::kBfChunks - 1 && c >= kQK / 32) break;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 kk = load_kw<KF>(st, lo, blk, k, w, m, sdelta);
+        const bf16x8 kk = load_kw<KF>(st, lo, blk, k);
         s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qo.b[k], s[blk], 0, 0, 0);
       }
     }
