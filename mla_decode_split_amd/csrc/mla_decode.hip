@@ -307,6 +307,8 @@ struct LaneOffs {
   int xw[2][2];
   int kr[2];
   int kb[2];
+  // E2M1 keys: E8M0 code -> fp32 scale (e8m0_f32 of every code, in LDS)
+  const __attribute__((address_space(3))) float* e8m0;
 
   __device__ inline void init(int m, int g, int w) {
     constexpr int R = Geom<KF>::kRow;
@@ -423,7 +425,7 @@ __device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q,
       } else {
         const uint32_t w = *(const uint32_t*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 64 * q);
         const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + pv_row(g, i) * kScaleRow + 4 * q + (m >> 2)];
-        x[i] = __builtin_bit_cast(u32x4, fp4x8_bf16(w, e8m0_f32(e)));
+        x[i] = __builtin_bit_cast(u32x4, fp4x8_bf16(w, lo.e8m0[e]));
       }
       if (MASK && pv_row(g, i) >= valid) x[i] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -694,7 +696,7 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, co
         // rope dims 512 + 32w + 8g + [0, 8), widened to bf16 with their block scale
         const uint32_t word = *(const uint32_t*)(st + lo.kr[blk]);
         const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + 16 + w];
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16(word, e8m0_f32(e)), qo.br, s[blk], 0, 0, 0);
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16(word, lo.e8m0[e]), qo.br, s[blk], 0, 0, 0);
       }
     }
   } else {
@@ -809,7 +811,8 @@ __device__ inline void set_priority(int prio) {
 }
 
 template <int QF, int KF>
-__device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, int64_t qrow, int64_t r0, int n, int32_t slot,
+__device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg,
+                            const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow, int64_t r0, int n, int32_t slot,
                             float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
   using G = Geom<KF>;
   constexpr int NS = G::kStages;
@@ -856,6 +859,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg, in
 
   LaneOffs<KF> lo;
   lo.init(m, g, w);
+  lo.e8m0 = e8m0_lut;
 
   QOperand<QF, KF> qop;
   qop.fetch(p.q, qrow, lane, w);
@@ -933,6 +937,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
   using G = Geom<KF>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[G::kLdsBytes];
   __shared__ f32x4 xchg[kXchgBytes / 16];
+  __shared__ float e8m0_lut[KF == DT_MXFP4 ? 256 : 1];
   int* counts = (int*)xchg;  // the sequence search runs before any exchange
 
   const int tid = threadIdx.x;
@@ -943,6 +948,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
 
   // Sequences overlapping [lo, hi): b in [#{j>=1: indptr[j] <= lo}, #{j<bs: indptr[j] < hi}).
   if (tid < 2) counts[tid] = 0;
+  if (KF == DT_MXFP4) e8m0_lut[tid] = e8m0_f32(tid);  // one code per thread (256 threads)
   __syncthreads();
   int c_first = 0, c_end = 0;
   for (int j = tid; j <= p.batch; j += G::kThreads) {
@@ -977,7 +983,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
-    split_piece<QF, KF>(p, ring, xchg, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
+    split_piece<QF, KF>(p, ring, xchg, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
     lds_barrier();  // the next piece refills the ring
   }
 }
