@@ -40,9 +40,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "cf98729a3a54230e0639c79a9de520399c4a66bd4b524cb55ccdc8d21f9437d4",
-    "fetch_kib": 153019.86,
-    "write_kib": 21148.49,
+    "source_sha256": "7642400ce4a0cbb0540bb515cb55d44b86d7e734177cf863f76aec32ff5fb21f",
+    "fetch_kib": 152145.54,
+    "write_kib": 16493.05,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
