@@ -68,7 +68,9 @@ typedef struct mla_problem {
 /* Optional planner overrides (NULL = planner's choice for every field). */
 typedef struct mla_plan_options {
   int32_t rows_per_split; /* > 0: KV rows each stage-1 workgroup takes (rounded up to 32) */
-  int32_t wgs_per_cu;     /* > 0: resident stage-1 workgroups per CU the planner targets */
+  int32_t wgs_per_cu;     /* > 0: stage-1 workgroups per CU the planner sizes the split for
+                             (default: as many as are resident together, 2 for bf16 and fp8
+                             KV, 3 for MXFP4 KV) */
 } mla_plan_options;
 
 /* What a plan decided (for tests, benchmarks and logs). */
@@ -82,6 +84,7 @@ typedef struct mla_plan_desc {
   int64_t workspace_bytes; /* bytes mla_decode_run needs */
   int32_t lds_bytes;       /* LDS per stage-1 workgroup */
   int32_t num_cus;         /* compute units planned for */
+  int32_t wgs_per_cu;      /* stage-1 workgroups per CU the plan is sized for (resident together) */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan;

@@ -70,21 +70,25 @@ enum Dt { DT_BF16 = MLA_DTYPE_BF16, DT_FP8 = MLA_DTYPE_FP8_E4M3FN, DT_MXFP4 = ML
 // A tile is 32 consecutive KV rows.  The four waves of a workgroup stream the
 // tiles of a piece through a shared ring of kStages LDS slots; a slot holds the
 // tile's rows and, for MXFP4, one 1 KB chunk with the tile's E8M0 scale bytes.
-// Two workgroups share a CU.
+// Two (fp8, bf16) or three (MXFP4) workgroups share a CU.
 
 template <int KF>
 struct KvGeom;
+// kWgsPerCu: resident workgroups per CU (one wave of each on every SIMD).  The
+// E2M1 tile is cheap to move and dear to compute, so three workgroups with
+// four-slot rings (which measured faster than two with seven); the fp8 and
+// bf16 tiles need their deeper rings to keep HBM busy, which leaves room for two.
 template <>
 struct KvGeom<DT_BF16> {
-  static constexpr int kRow = 2 * kQK, kStages = 2, kScaleChunks = 0, kDmaWaves = 4;
+  static constexpr int kRow = 2 * kQK, kStages = 2, kScaleChunks = 0, kDmaWaves = 4, kWgsPerCu = 2;
 };
 template <>
 struct KvGeom<DT_FP8> {
-  static constexpr int kRow = kQK, kStages = 4, kScaleChunks = 0, kDmaWaves = 4;
+  static constexpr int kRow = kQK, kStages = 4, kScaleChunks = 0, kDmaWaves = 4, kWgsPerCu = 2;
 };
 template <>
 struct KvGeom<DT_MXFP4> {
-  static constexpr int kRow = kQK / 2, kStages = 7, kScaleChunks = 1, kDmaWaves = 3;
+  static constexpr int kRow = kQK / 2, kStages = 4, kScaleChunks = 1, kDmaWaves = 3, kWgsPerCu = 3;
 };
 
 template <int KF>
@@ -104,7 +108,9 @@ struct Geom {
   static constexpr int kStageBytes = kChunks * 1024;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static_assert(kRowBytes % 1024 == 0, "a tile must fill whole DMA chunks");
-  static_assert(2 * (kLdsBytes + 4 * 2 * 64 * 16) <= 160 * 1024, "two workgroups per CU (ring + score exchange)");
+  static constexpr int kWgsPerCu = KvGeom<KF>::kWgsPerCu;
+  static_assert(kWgsPerCu * (kLdsBytes + 4 * 2 * 64 * 16 + (KF == DT_MXFP4 ? 1024 : 0)) <= 160 * 1024,
+                "resident workgroups per CU (ring + score exchange + E8M0 table)");
   static_assert((kStages - 2) * kMaxChunksPerWave <= 63, "vmcnt range");
   __host__ __device__ static constexpr int chunks_of_wave(int w) {
     return w < kDmaWaves ? (kChunks - w + kDmaWaves - 1) / kDmaWaves : 0;
@@ -215,6 +221,15 @@ __device__ inline void wait_tiles_behind(int chunks, int k) {
     wait_tiles_behind_n<MAXC>(k);
   else
     wait_tiles_behind_n<(MAXC > 1 ? MAXC - 1 : 1)>(k);
+}
+
+// The same with k fixed at compile time (one branch on the chunk count).
+template <int MAXC, int K>
+__device__ inline void wait_tiles_behind_fixed(int chunks) {
+  if (chunks == MAXC)
+    wait_vmcnt_clamped<K * MAXC>();
+  else
+    wait_vmcnt_clamped<K * (MAXC > 1 ? MAXC - 1 : 1)>();
 }
 
 // Workgroup barrier that also drains this wave's LDS traffic; the memory
@@ -719,94 +734,135 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, co
   }
 }
 
-// Softmax state of one piece, identical in the four waves of the workgroup
-// except for acc: running max (base 2) per head, the lane's part of the
-// running sum, and O^T for the wave's 128 value columns: acc[j][r] = column
-// 128w + 32g + 8r + j of head lane & 15.
+// Softmax state of one piece.  m_run (the running maximum, base 2, per head)
+// is identical in the four waves; l_run is the lane's part of the running sum
+// over the tokens this wave takes the softmax of; acc is O^T for the wave's
+// 128 value columns: acc[j][r] = column 128w + 32g + 8r + j of head lane & 15.
 struct WaveState {
   float m_run;
   float l_run;
   f32x4 acc[8];
 };
 
-// Partial-score exchange buffer: [wave][block][lane] f32x4.
-constexpr int kXchgBytes = 4 * 2 * 64 * 16;
+// Partial-score exchange buffer, one plane per token of a lane's f32x4:
+// [wave][block][r][lane] floats, so the wave that finishes the scores of
+// component r reads 64 consecutive floats per (wave, block).
+constexpr int kXchgBytes = 4 * 2 * 4 * 64 * 4;
 
+// 16-byte units of a tile row that hold the rope dims (used only by S = Q K^T):
+// once every wave has its partial scores, the current tile's rope units carry
+// the probability exchange.
+template <int KF>
+struct RopeUnits;
+template <>
+struct RopeUnits<DT_FP8> {
+  static constexpr int kFirst = 32, kCount = 4;
+};
+template <>
+struct RopeUnits<DT_BF16> {
+  static constexpr int kFirst = 64, kCount = 8;
+};
+template <>
+struct RopeUnits<DT_MXFP4> {
+  static constexpr int kFirst = 16, kCount = 2;
+};
+
+// LDS byte offsets (within a tile slot) of the probability exchange:
+//   P slot of lane l (16 bytes): bf16 P of the eight tokens lane l feeds to the
+//     PV product, [block][wave] - row l >> 1, rope unit (l & 1);
+//   max slot of head h (16 bytes): the four waves' maxima of the head's scores.
+template <int KF>
+__device__ inline int p_slot(int lane) {
+  constexpr int R = Geom<KF>::kRow;
+  const int row = lane >> 1;
+  return row * R + 16 * ((RopeUnits<KF>::kFirst + (lane & 1)) ^ Layout<KF>::swz(row));
+}
+template <int KF>
+__device__ inline int max_slot(int h) {
+  constexpr int R = Geom<KF>::kRow;
+  if constexpr (RopeUnits<KF>::kCount >= 4)
+    return h * R + 16 * ((RopeUnits<KF>::kFirst + 2) ^ Layout<KF>::swz(h));
+  else  // E2M1 rows have two rope units: the unused tail of the tile's scale chunk
+    return Geom<KF>::kRowBytes + 768 + 16 * h;
+}
+
+// One tile: S^T partials (this wave's share of the 576 dims) -> LDS; the full
+// scores of this wave's tokens 4g + w and 16 + 4g + w (head m) -> their
+// probabilities relative to the running maximum -> LDS; every wave then takes
+// the eight probabilities its PV lanes need and multiplies them into its 128
+// value columns.  When a score exceeds the running maximum by more than
+// kRescaleSlack (decided from the four waves' per-head maxima, so uniformly),
+// the maximum is raised to the tile's, the accumulators rescaled and the
+// probabilities recomputed and exchanged again.  Below the slack
+// p = 2^(t - m_run) <= 2^kRescaleSlack, which bf16 P and the fp32 sums hold
+// without loss, and the final normalisation by the running sum is unchanged.
 template <int QF, int KF, bool MASK>
-__device__ inline void process_tile(const uint8_t* st, f32x4* xchg, const QOperand<QF, KF>& qo,
-                                    const LaneOffs<KF>& lo, WaveState& ws, int w, int m, int g, int sdelta, int valid,
-                                    float score_scale) {
+__device__ inline void process_tile(uint8_t* st, float* xchg, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo,
+                                    WaveState& ws, int w, int m, int g, int sdelta, int valid, float score_scale) {
   const int lane = threadIdx.x & 63;
   {
     f32x4 part[2];
     qk_tile<QF, KF>(st, qo, lo, w, m, sdelta, part);
-    xchg[(2 * w + 0) * 64 + lane] = part[0];
-    xchg[(2 * w + 1) * 64 + lane] = part[1];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xchg[((2 * w + blk) * 4 + r) * 64 + lane] = part[blk][r];
   }
-  lds_barrier();  // every wave's partial scores are in LDS
-  f32x4 s[2];
+  lds_barrier();  // every wave's partial scores are in LDS and every wave is done with the rope dims
+  // raw scores of tokens 4g + w (block 0) and 16 + 4g + w (block 1), summed in wave order
+  float sv[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    // same summation order in every wave, so all four see identical scores
-    s[blk] = xchg[(0 + blk) * 64 + lane];
-    s[blk] += xchg[(2 + blk) * 64 + lane];
-    s[blk] += xchg[(4 + blk) * 64 + lane];
-    s[blk] += xchg[(6 + blk) * 64 + lane];
+    float t = xchg[((0 + blk) * 4 + w) * 64 + lane];
+    t += xchg[((2 + blk) * 4 + w) * 64 + lane];
+    t += xchg[((4 + blk) * 4 + w) * 64 + lane];
+    t += xchg[((6 + blk) * 4 + w) * 64 + lane];
+    sv[blk] = t;
+    if (MASK && 16 * blk + 4 * g + w >= valid) sv[blk] = -INFINITY;
   }
-  // raw sums; the base-2 score is sv * c with c > 0 (so max(sv) * c is the max score)
+  // the base-2 score is sv * c with c > 0, so the maximum is taken on the raw sums
   const float c = score_scale * qo.scale;
-  float sv[8];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    sv[k] = s[k >> 2][k & 3];
-    if (MASK && pv_row(g, k) >= valid) sv[k] = -INFINITY;
-    mx = fmaxf(mx, sv[k]);
-  }
+  float mx = fmaxf(sv[0], sv[1]);
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
   mx *= c;
-  // The reference max m_run is raised (to the exact head-wide maximum) and the
-  // accumulators rescaled only when a score exceeds it by more than
-  // kRescaleSlack; otherwise p = 2^(t - m_run) <= 2^kRescaleSlack, which bf16
-  // P and the fp32 sums hold without loss, and the final normalisation by the
-  // running sum is unchanged.  Both waves see the same scores, so they take
-  // the same decisions.
-  if (__builtin_amdgcn_ballot_w64(mx > ws.m_run + kRescaleSlack) != 0) {
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(ws.m_run, mx);
+  uint8_t* ps = st + p_slot<KF>(lane);
+  auto post_p = [&](float p0, float p1) {
+    *(__bf16*)(ps + 2 * w) = (__bf16)p0;
+    *(__bf16*)(ps + 8 + 2 * w) = (__bf16)p1;
+  };
+  float p0 = __builtin_amdgcn_exp2f(fmaf(sv[0], c, -ws.m_run));
+  float p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], c, -ws.m_run));
+  post_p(p0, p1);
+  if (g == 0) *(float*)(st + max_slot<KF>(m) + 4 * w) = mx;
+  lds_barrier();  // every wave's probabilities and maxima are in LDS
+  const f32x4 mw = *(const f32x4*)(st + max_slot<KF>(m));
+  const float tmax = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+  if (__builtin_amdgcn_ballot_w64(tmax > ws.m_run + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(ws.m_run, tmax);
     const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
     ws.m_run = m_new;
     ws.l_run *= alpha;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ws.acc[j] *= alpha;
+    p0 = __builtin_amdgcn_exp2f(fmaf(sv[0], c, -ws.m_run));
+    p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], c, -ws.m_run));
+    post_p(p0, p1);
+    lds_barrier();  // the probabilities against the new maximum are in LDS
   }
-  uint32_t pk[4];
-  float ps = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * k], c, -ws.m_run));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * k + 1], c, -ws.m_run));
-    ps += p0 + p1;
-    pk[k] = pack_bf16x2(p0, p1);
-  }
-  ws.l_run += ps;
-  const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+  ws.l_run += p0 + p1;
+  const bf16x8 pb = __builtin_bit_cast(bf16x8, *(const u32x4*)ps);
   bf16x8 va[8];
   load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
 #pragma unroll
   for (int j = 0; j < 8; ++j) ws.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, ws.acc[j], 0, 0, 0);
 }
 
-// Two workgroups share each CU, and the SIMD arbiter favours older waves, so
-// with equal priorities the workgroup dispatched second falls behind and the
-// kernel waits for it.  Each wave's priority instead follows how much of its
+// Workgroups share each CU, and the SIMD arbiter favours older waves, so with
+// equal priorities the workgroups dispatched later fall behind and the kernel
+// waits for them.  Each wave's priority instead follows how much of its
 // workgroup's row range is left (3 above one half, 2 above a quarter, 1 above
 // an eighth, else 0): whichever workgroup lags is favoured until it catches up.
-__device__ inline int range_priority(int64_t remaining, int32_t range_rows) {
-  const int64_t r = remaining * 8;
-  return r > 4 * (int64_t)range_rows ? 3 : r > 2 * (int64_t)range_rows ? 2 : r > range_rows ? 1 : 0;
-}
-
 __device__ inline void set_priority(int prio) {
   switch (prio) {
     case 3: __builtin_amdgcn_s_setprio(3); break;
@@ -817,7 +873,7 @@ __device__ inline void set_priority(int prio) {
 }
 
 template <int QF, int KF>
-__device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg,
+__device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg,
                             const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow, int64_t r0, int n, int32_t slot,
                             float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
   using G = Geom<KF>;
@@ -873,7 +929,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg,
   qop.arrive();
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
-  qop.prepare((float*)xchg + 256, w, lane);  // clear of the sequence counts at the start of xchg
+  qop.prepare(xchg + 256, w, lane);  // clear of the sequence counts at the start of xchg
   qop.settle();
 
   WaveState ws;
@@ -885,7 +941,12 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg,
   const int my_chunks = G::chunks_of_wave(w);
   // tile i is complete in LDS and every wave is done with tile i - 1
   auto advance = [&](int i) {
-    if (my_chunks > 0) wait_tiles_behind<G::kMaxChunksPerWave>(my_chunks, std::min(NS - 2, ntiles - 1 - i));
+    if (my_chunks > 0) {
+      if (i + NS - 2 < ntiles)  // the usual case: the NS - 2 tiles after tile i stay in flight
+        wait_tiles_behind_fixed<G::kMaxChunksPerWave, NS - 2>(my_chunks);
+      else
+        wait_tiles_behind<G::kMaxChunksPerWave>(my_chunks, ntiles - 1 - i);
+    }
     lds_barrier();
     if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
   };
@@ -895,9 +956,15 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg,
   // full tiles in the loop (one code path, so the accumulators stay in place);
   // a partial last tile after it
   const int nfull = n / kTile;
+  // priority 3 while more than half the range is left, 2 above a quarter, 1
+  // above an eighth: with rows_left(i) = wg_hi - (r0 + 32 i), 8 rows_left(i) > x
+  // exactly when i < below(x)
+  const int64_t d8 = 8 * (wg_hi - r0);
+  auto below = [&](int64_t x) -> int { return d8 > x ? (int)std::min<int64_t>((d8 - x + 255) / 256, INT_MAX) : 0; };
+  const int f4 = below(4 * (int64_t)wg_rows), f2 = below(2 * (int64_t)wg_rows), f1 = below(wg_rows);
   int prio = -1;
   for (int i = 0; i < nfull; ++i) {
-    const int want = range_priority(wg_hi - (r0 + (int64_t)i * kTile), wg_rows);
+    const int want = (i < f4) + (i < f2) + (i < f1);
     if (want != prio) {
       prio = want;
       set_priority(prio);
@@ -913,8 +980,13 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg,
   }
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
+  // running sum: this wave's tokens (over the lane groups), then over the waves
+  // (every wave is past its last read of the score planes)
   float lt = ws.l_run + shfl_xor(ws.l_run, 16);
   lt += shfl_xor(lt, 32);
+  if (g == 0) xchg[16 * w + m] = lt;
+  lds_barrier();
+  lt = xchg[m] + xchg[16 + m] + xchg[32 + m] + xchg[48 + m];
   const float inv = out_scale / lt;
   const int col0 = 128 * w + 32 * g;
   if (slot < 0) {
@@ -939,11 +1011,11 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, f32x4* xchg,
 }
 
 template <int QF, int KF>
-__global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_split_kernel(
+__global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(Geom<KF>::kWgsPerCu, Geom<KF>::kWgsPerCu))) void mla_split_kernel(
     SplitParams p) {
   using G = Geom<KF>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[G::kLdsBytes];
-  __shared__ f32x4 xchg[kXchgBytes / 16];
+  __shared__ float xchg[kXchgBytes / 4];
   __shared__ float e8m0_lut[KF == DT_MXFP4 ? 256 : 1];
   int* counts = (int*)xchg;  // the sequence search runs before any exchange
 
@@ -1127,6 +1199,7 @@ struct mla_plan {
   int32_t lds_bytes;
   int32_t stage2;
   int32_t num_cus;
+  int32_t wgs_per_cu;
   size_t ws_bytes;
   size_t lse_offset;
 };
@@ -1152,7 +1225,15 @@ int lds_bytes_for(int kv_dtype) {
   switch (kv_dtype) {
     case DT_BF16: return Geom<DT_BF16>::kLdsBytes + kXchgBytes;
     case DT_FP8: return Geom<DT_FP8>::kLdsBytes + kXchgBytes;
-    default: return Geom<DT_MXFP4>::kLdsBytes + kXchgBytes;
+    default: return Geom<DT_MXFP4>::kLdsBytes + kXchgBytes + 256 * 4;  // + the E8M0 table
+  }
+}
+
+int wgs_per_cu_for(int kv_dtype) {
+  switch (kv_dtype) {
+    case DT_BF16: return Geom<DT_BF16>::kWgsPerCu;
+    case DT_FP8: return Geom<DT_FP8>::kWgsPerCu;
+    default: return Geom<DT_MXFP4>::kWgsPerCu;
   }
 }
 
@@ -1220,7 +1301,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   }
 
   const int64_t total = pr->total_kv;
-  const int wpc = (opt && opt->wgs_per_cu > 0) ? opt->wgs_per_cu : 2;
+  const int wpc = (opt && opt->wgs_per_cu > 0) ? opt->wgs_per_cu : wgs_per_cu_for(pr->kv_dtype);
   int64_t R;
   if (opt && opt->rows_per_split > 0) {
     R = opt->rows_per_split;
@@ -1251,6 +1332,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   pl->lds_bytes = lds_bytes_for(pr->kv_dtype);
   pl->stage2 = stage2 ? 1 : 0;
   pl->num_cus = num_cus;
+  pl->wgs_per_cu = wpc;
   const size_t slots = 2 * (size_t)G;
   const size_t o_bytes = slots * kHeads * kV * sizeof(float);
   pl->lse_offset = (o_bytes + 255) / 256 * 256;
@@ -1273,6 +1355,7 @@ mla_status mla_decode_plan_describe(const mla_plan* pl, mla_plan_desc* d) {
   d->workspace_bytes = (int64_t)pl->ws_bytes;
   d->lds_bytes = pl->lds_bytes;
   d->num_cus = pl->num_cus;
+  d->wgs_per_cu = pl->wgs_per_cu;
   return MLA_OK;
 }
 

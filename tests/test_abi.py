@@ -61,7 +61,8 @@ def test_plans_for_the_five_workloads(name):
     assert d["num_splits"] * d["rows_per_split"] >= ind[-1] > (d["num_splits"] - 1) * d["rows_per_split"]
     assert d["rows_per_split"] % d["tile_rows"] == 0
     assert d["partial_slots"] == 2 * d["num_splits"]
-    assert d["lds_bytes"] * 2 <= 160 * 1024
+    assert d["lds_bytes"] * d["wgs_per_cu"] <= 160 * 1024  # that many workgroups fit a CU's LDS
+    assert d["wgs_per_cu"] == (3 if spec["kv_dtype"] == "mxfp4" else 2)
     assert plan.workspace_bytes >= d["partial_slots"] * 16 * 513 * 4
     _check_cut(plan, ind)
 
