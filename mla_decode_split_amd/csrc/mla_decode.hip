@@ -770,7 +770,8 @@ struct RopeUnits<DT_MXFP4> {
 // LDS byte offsets (within a tile slot) of the probability exchange:
 //   P slot of lane l (16 bytes): bf16 P of the eight tokens lane l feeds to the
 //     PV product, [block][wave] - row l >> 1, rope unit (l & 1);
-//   max slot of head h (16 bytes): the four waves' maxima of the head's scores.
+//   max slot of head h (16 bytes): the four waves' maxima of the head's scores;
+//   flag slot (16 bytes): per wave, whether a score passed the rescale slack.
 template <int KF>
 __device__ inline int p_slot(int lane) {
   constexpr int R = Geom<KF>::kRow;
@@ -785,24 +786,34 @@ __device__ inline int max_slot(int h) {
   else  // E2M1 rows have two rope units: the unused tail of the tile's scale chunk
     return Geom<KF>::kRowBytes + 768 + 16 * h;
 }
+template <int KF>
+__device__ inline int flag_slot() {
+  if constexpr (RopeUnits<KF>::kCount >= 4)
+    return 16 * ((RopeUnits<KF>::kFirst + 3) ^ Layout<KF>::swz(0));
+  else
+    return Geom<KF>::kRowBytes + 704;
+}
 
 // One tile: S^T partials (this wave's share of the 576 dims) -> LDS; the full
 // scores of this wave's tokens 4g + w and 16 + 4g + w (head m) -> their
 // probabilities relative to the running maximum -> LDS; every wave then takes
 // the eight probabilities its PV lanes need and multiplies them into its 128
-// value columns.  When a score exceeds the running maximum by more than
-// kRescaleSlack (decided from the four waves' per-head maxima, so uniformly),
-// the maximum is raised to the tile's, the accumulators rescaled and the
-// probabilities recomputed and exchanged again.  Below the slack
-// p = 2^(t - m_run) <= 2^kRescaleSlack, which bf16 P and the fp32 sums hold
-// without loss, and the final normalisation by the running sum is unchanged.
+// value columns.  When a probability would exceed 2^kRescaleSlack (any wave
+// may see it; the four waves' flags make the decision uniform), the maximum
+// is raised to the tile's, the accumulators are rescaled and the
+// probabilities recomputed and exchanged again.  Below the slack bf16 P and
+// the fp32 sums hold p = 2^(t - m_run) without loss, and the final
+// normalisation by the running sum is unchanged.
 template <int QF, int KF, bool MASK>
 __device__ inline void process_tile(uint8_t* st, float* xchg, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo,
                                     WaveState& ws, int w, int m, int g, int sdelta, int valid, float score_scale) {
   const int lane = threadIdx.x & 63;
+  bf16x8 va[8];
   {
     f32x4 part[2];
     qk_tile<QF, KF>(st, qo, lo, w, m, sdelta, part);
+    // V^T operands do not depend on the scores: read them while the products finish
+    load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -820,25 +831,31 @@ __device__ inline void process_tile(uint8_t* st, float* xchg, const QOperand<QF,
     sv[blk] = t;
     if (MASK && 16 * blk + 4 * g + w >= valid) sv[blk] = -INFINITY;
   }
-  // the base-2 score is sv * c with c > 0, so the maximum is taken on the raw sums
+  // the base-2 score is sv * c with c > 0
   const float c = score_scale * qo.scale;
-  float mx = fmaxf(sv[0], sv[1]);
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  mx *= c;
   uint8_t* ps = st + p_slot<KF>(lane);
   auto post_p = [&](float p0, float p1) {
     *(__bf16*)(ps + 2 * w) = (__bf16)p0;
     *(__bf16*)(ps + 8 + 2 * w) = (__bf16)p1;
   };
-  float p0 = __builtin_amdgcn_exp2f(fmaf(sv[0], c, -ws.m_run));
-  float p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], c, -ws.m_run));
+  const float t0 = fmaf(sv[0], c, -ws.m_run), t1 = fmaf(sv[1], c, -ws.m_run);
+  float p0 = __builtin_amdgcn_exp2f(t0);
+  float p1 = __builtin_amdgcn_exp2f(t1);
   post_p(p0, p1);
-  if (g == 0) *(float*)(st + max_slot<KF>(m) + 4 * w) = mx;
-  lds_barrier();  // every wave's probabilities and maxima are in LDS
-  const f32x4 mw = *(const f32x4*)(st + max_slot<KF>(m));
-  const float tmax = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-  if (__builtin_amdgcn_ballot_w64(tmax > ws.m_run + kRescaleSlack) != 0) {
+  const bool big = __builtin_amdgcn_ballot_w64(t0 > kRescaleSlack || t1 > kRescaleSlack) != 0;
+  int* flags = (int*)(st + flag_slot<KF>());
+  if (lane == 0) flags[w] = big ? 1 : 0;
+  lds_barrier();  // every wave's probabilities and flag are in LDS
+  const u32x4 fl = *(const u32x4*)flags;
+  if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0u) {
+    // tile maximum per head: this wave's tokens (over the lane groups), then the waves
+    float mx = fmaxf(sv[0], sv[1]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    if (g == 0) *(float*)(st + max_slot<KF>(m) + 4 * w) = mx * c;
+    lds_barrier();
+    const f32x4 mw = *(const f32x4*)(st + max_slot<KF>(m));
+    const float tmax = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
     const float m_new = fmaxf(ws.m_run, tmax);
     const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
     ws.m_run = m_new;
@@ -852,8 +869,6 @@ __device__ inline void process_tile(uint8_t* st, float* xchg, const QOperand<QF,
   }
   ws.l_run += p0 + p1;
   const bf16x8 pb = __builtin_bit_cast(bf16x8, *(const u32x4*)ps);
-  bf16x8 va[8];
-  load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
 #pragma unroll
   for (int j = 0; j < 8; ++j) ws.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, ws.acc[j], 0, 0, 0);
 }
