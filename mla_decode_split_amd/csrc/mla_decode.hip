@@ -794,62 +794,71 @@ __device__ inline int flag_slot() {
     return Geom<KF>::kRowBytes + 704;
 }
 
-// One tile: S^T partials (this wave's share of the 576 dims) -> LDS; the full
-// scores of this wave's tokens 4g + w and 16 + 4g + w (head m) -> their
-// probabilities relative to the running maximum -> LDS; every wave then takes
-// the eight probabilities its PV lanes need and multiplies them into its 128
-// value columns.  When a probability would exceed 2^kRescaleSlack (any wave
-// may see it; the four waves' flags make the decision uniform), the maximum
-// is raised to the tile's, the accumulators are rescaled and the
-// probabilities recomputed and exchanged again.  Below the slack bf16 P and
-// the fp32 sums hold p = 2^(t - m_run) without loss, and the final
-// normalisation by the running sum is unchanged.
+// A tile goes through two steps, one ring barrier apart, so that every tile
+// costs two workgroup barriers and the products of consecutive tiles overlap:
+//
+// score_tile: S^T partials (this wave's share of the 576 dims) -> LDS; after
+//   the exchange barrier, the full scores of this wave's tokens 4g + w and
+//   16 + 4g + w (head m) and their probabilities relative to the running
+//   maximum -> the tile's rope bytes (no wave reads them after the exchange),
+//   with a per-wave flag: some probability would exceed 2^kRescaleSlack.
+// finish_tile (after the next barrier): when any wave flagged, the maximum is
+//   raised to the tile's, the accumulators rescaled and the probabilities
+//   recomputed and exchanged again (rare: the first tile, and a score well above
+//   all before it); then every wave takes the eight probabilities its PV lanes
+//   need and multiplies them into its 128 value columns.
+// Below the slack bf16 P and the fp32 sums hold p = 2^(t - m_run) without loss,
+// and the final normalisation by the running sum is unchanged.
+struct TileScores {
+  float sv[2];  // raw scores of tokens 4g + w and 16 + 4g + w, head m (-inf when masked)
+  float p[2];   // their probabilities against m_run as it was when they were posted
+};
+
 template <int QF, int KF, bool MASK>
-__device__ inline void process_tile(uint8_t* st, float* xchg, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo,
-                                    WaveState& ws, int w, int m, int g, int sdelta, int valid, float score_scale) {
+__device__ inline void score_tile(uint8_t* st, float* xchg, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo,
+                                  const WaveState& ws, int w, int m, int g, int sdelta, int valid, float c,
+                                  TileScores& ts) {
   const int lane = threadIdx.x & 63;
-  bf16x8 va[8];
   {
     f32x4 part[2];
     qk_tile<QF, KF>(st, qo, lo, w, m, sdelta, part);
-    // V^T operands do not depend on the scores: read them while the products finish
-    load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) xchg[((2 * w + blk) * 4 + r) * 64 + lane] = part[blk][r];
   }
   lds_barrier();  // every wave's partial scores are in LDS and every wave is done with the rope dims
-  // raw scores of tokens 4g + w (block 0) and 16 + 4g + w (block 1), summed in wave order
-  float sv[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
+    // summed in wave order
     float t = xchg[((0 + blk) * 4 + w) * 64 + lane];
     t += xchg[((2 + blk) * 4 + w) * 64 + lane];
     t += xchg[((4 + blk) * 4 + w) * 64 + lane];
     t += xchg[((6 + blk) * 4 + w) * 64 + lane];
-    sv[blk] = t;
-    if (MASK && 16 * blk + 4 * g + w >= valid) sv[blk] = -INFINITY;
+    ts.sv[blk] = (MASK && 16 * blk + 4 * g + w >= valid) ? -INFINITY : t;
   }
   // the base-2 score is sv * c with c > 0
-  const float c = score_scale * qo.scale;
+  const float t0 = fmaf(ts.sv[0], c, -ws.m_run), t1 = fmaf(ts.sv[1], c, -ws.m_run);
+  ts.p[0] = __builtin_amdgcn_exp2f(t0);
+  ts.p[1] = __builtin_amdgcn_exp2f(t1);
   uint8_t* ps = st + p_slot<KF>(lane);
-  auto post_p = [&](float p0, float p1) {
-    *(__bf16*)(ps + 2 * w) = (__bf16)p0;
-    *(__bf16*)(ps + 8 + 2 * w) = (__bf16)p1;
-  };
-  const float t0 = fmaf(sv[0], c, -ws.m_run), t1 = fmaf(sv[1], c, -ws.m_run);
-  float p0 = __builtin_amdgcn_exp2f(t0);
-  float p1 = __builtin_amdgcn_exp2f(t1);
-  post_p(p0, p1);
+  *(__bf16*)(ps + 2 * w) = (__bf16)ts.p[0];
+  *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts.p[1];
   const bool big = __builtin_amdgcn_ballot_w64(t0 > kRescaleSlack || t1 > kRescaleSlack) != 0;
-  int* flags = (int*)(st + flag_slot<KF>());
-  if (lane == 0) flags[w] = big ? 1 : 0;
-  lds_barrier();  // every wave's probabilities and flag are in LDS
-  const u32x4 fl = *(const u32x4*)flags;
+  if (lane == 0) ((int*)(st + flag_slot<KF>()))[w] = big ? 1 : 0;
+}
+
+template <int QF, int KF, bool MASK>
+__device__ inline void finish_tile(uint8_t* st, const LaneOffs<KF>& lo, WaveState& ws, int w, int m, int g,
+                                   int sdelta, int valid, float c, TileScores& ts) {
+  const int lane = threadIdx.x & 63;
+  uint8_t* ps = st + p_slot<KF>(lane);
+  bf16x8 va[8];
+  load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
+  const u32x4 fl = *(const u32x4*)(st + flag_slot<KF>());
   if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0u) {
     // tile maximum per head: this wave's tokens (over the lane groups), then the waves
-    float mx = fmaxf(sv[0], sv[1]);
+    float mx = fmaxf(ts.sv[0], ts.sv[1]);
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     if (g == 0) *(float*)(st + max_slot<KF>(m) + 4 * w) = mx * c;
@@ -862,12 +871,13 @@ __device__ inline void process_tile(uint8_t* st, float* xchg, const QOperand<QF,
     ws.l_run *= alpha;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ws.acc[j] *= alpha;
-    p0 = __builtin_amdgcn_exp2f(fmaf(sv[0], c, -ws.m_run));
-    p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], c, -ws.m_run));
-    post_p(p0, p1);
+    ts.p[0] = __builtin_amdgcn_exp2f(fmaf(ts.sv[0], c, -ws.m_run));
+    ts.p[1] = __builtin_amdgcn_exp2f(fmaf(ts.sv[1], c, -ws.m_run));
+    *(__bf16*)(ps + 2 * w) = (__bf16)ts.p[0];
+    *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts.p[1];
     lds_barrier();  // the probabilities against the new maximum are in LDS
   }
-  ws.l_run += p0 + p1;
+  ws.l_run += ts.p[0] + ts.p[1];
   const bf16x8 pb = __builtin_bit_cast(bf16x8, *(const u32x4*)ps);
 #pragma unroll
   for (int j = 0; j < 8; ++j) ws.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, ws.acc[j], 0, 0, 0);
@@ -963,6 +973,11 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg,
         wait_tiles_behind<G::kMaxChunksPerWave>(my_chunks, ntiles - 1 - i);
     }
     lds_barrier();
+  };
+  // The DMA of tile i + NS - 1 (into the slot tile i - 1 left) goes out after
+  // tile i's products are issued: when the memory pipeline is full the issue
+  // waits for room, and there it waits while the matrix cores work.
+  auto refill = [&](int i) {
     if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
   };
   auto sdelta_of = [&](int i) {
@@ -978,21 +993,42 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg,
   auto below = [&](int64_t x) -> int { return d8 > x ? (int)std::min<int64_t>((d8 - x + 255) / 256, INT_MAX) : 0; };
   const int f4 = below(4 * (int64_t)wg_rows), f2 = below(2 * (int64_t)wg_rows), f1 = below(wg_rows);
   int prio = -1;
-  for (int i = 0; i < nfull; ++i) {
+  auto priority = [&](int i) {
     const int want = (i < f4) + (i < f2) + (i < f1);
     if (want != prio) {
       prio = want;
       set_priority(prio);
     }
+  };
+  const float c = score_scale * qop.scale;
+  const int last_valid = n - (ntiles - 1) * kTile;
+  auto stage = [&](int i) { return ring + (i % NS) * G::kStageBytes; };
+  TileScores ts;
+  // tile 0, then for each later tile: its scores and the previous tile's products
+  priority(0);
+  advance(0);
+  if (nfull > 0)
+    score_tile<QF, KF, false>(stage(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), kTile, c, ts);
+  else
+    score_tile<QF, KF, true>(stage(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), last_valid, c, ts);
+  refill(0);
+  for (int i = 1; i < nfull; ++i) {
+    priority(i);
     advance(i);
-    process_tile<QF, KF, false>(ring + (i % NS) * G::kStageBytes, xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile,
-                                score_scale);
+    finish_tile<QF, KF, false>(stage(i - 1), lo, ws, w, m, g, sdelta_of(i - 1), kTile, c, ts);
+    score_tile<QF, KF, false>(stage(i), xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile, c, ts);
+    refill(i);
   }
-  if (nfull < ntiles) {
+  if (nfull > 0 && nfull < ntiles) {  // the partial last tile
     advance(nfull);
-    process_tile<QF, KF, true>(ring + (nfull % NS) * G::kStageBytes, xchg, qop, lo, ws, w, m, g, sdelta_of(nfull),
-                               n - nfull * kTile, score_scale);
+    finish_tile<QF, KF, false>(stage(nfull - 1), lo, ws, w, m, g, sdelta_of(nfull - 1), kTile, c, ts);
+    score_tile<QF, KF, true>(stage(nfull), xchg, qop, lo, ws, w, m, g, sdelta_of(nfull), last_valid, c, ts);
   }
+  lds_barrier();  // the last tile's probabilities are in LDS
+  if (nfull < ntiles)
+    finish_tile<QF, KF, true>(stage(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1), last_valid, c, ts);
+  else
+    finish_tile<QF, KF, false>(stage(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1), kTile, c, ts);
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
   // running sum: this wave's tokens (over the lane groups), then over the waves
