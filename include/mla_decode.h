@@ -79,7 +79,8 @@ typedef struct mla_plan_desc {
   int32_t rows_per_split;  /* R, a multiple of tile_rows */
   int32_t tile_rows;       /* KV rows per LDS tile */
   int32_t stages;          /* depth of the LDS tile ring */
-  int32_t partial_slots;   /* 2*G partial (O, LSE) slots in the workspace */
+  int32_t partial_slots;   /* 2*G partial (O, LSE) slots in the workspace: O as bf16 [16][512]
+                              (normalised by its own running sum), LSE as fp32 [16] */
   int32_t stage2;          /* 1 if mla_decode_run launches the LSE-merge kernel */
   int64_t workspace_bytes; /* bytes mla_decode_run needs */
   int32_t lds_bytes;       /* LDS per stage-1 workgroup */

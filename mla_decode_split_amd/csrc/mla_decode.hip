@@ -474,7 +474,7 @@ struct SplitParams {
   const int32_t* qo_indptr;
   const int32_t* kv_indptr;
   uint16_t* out;
-  float* part_o;
+  uint16_t* part_o;
   float* part_lse;
   int64_t total_kv;
   int32_t total_q;
@@ -1040,21 +1040,16 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg,
   lt = xchg[m] + xchg[16 + m] + xchg[32 + m] + xchg[48 + m];
   const float inv = out_scale / lt;
   const int col0 = 128 * w + 32 * g;
-  if (slot < 0) {
-    uint16_t* o = p.out + (qrow * kHeads + m) * kV + col0;
+  {
+    // whole sequence: the output; piece of a split one: its partial O, also bf16 (the
+    // merge adds at most one bf16 rounding of the weighted terms to the output's own)
+    uint16_t* o = (slot < 0 ? p.out + (qrow * kHeads + m) * kV : p.part_o + ((int64_t)slot * kHeads + m) * kV) + col0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       u32x4 v;
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[k] = pack_bf16x2(ws.acc[2 * k][r] * inv, ws.acc[2 * k + 1][r] * inv);
       *(u32x4*)(o + 8 * r) = v;
-    }
-  } else {
-    float* o = p.part_o + ((int64_t)slot * kHeads + m) * kV + col0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *(f32x4*)(o + 8 * r) = f32x4{ws.acc[0][r] * inv, ws.acc[1][r] * inv, ws.acc[2][r] * inv, ws.acc[3][r] * inv};
-      *(f32x4*)(o + 8 * r + 4) = f32x4{ws.acc[4][r] * inv, ws.acc[5][r] * inv, ws.acc[6][r] * inv, ws.acc[7][r] * inv};
     }
   }
   if (slot >= 0 && w == 0 && g == 0)
@@ -1121,7 +1116,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
 // ---------------------------------------------------------------- stage 2
 
 struct MergeParams {
-  const float* part_o;
+  const uint16_t* part_o;
   const float* part_lse;
   const int32_t* qo_indptr;
   const int32_t* kv_indptr;
@@ -1166,7 +1161,8 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p) {
       if (base + k <= g1) {
         const int64_t slot = merge_slot(base + k, g0);
         lse[k] = p.part_lse[slot * kHeads + h];
-        v[k] = *(const f32x4*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
+        const uint2 u = *(const uint2*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
+        v[k] = f32x4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
       }
     }
     float mx = m_run;
@@ -1385,7 +1381,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   pl->num_cus = num_cus;
   pl->wgs_per_cu = wpc;
   const size_t slots = 2 * (size_t)G;
-  const size_t o_bytes = slots * kHeads * kV * sizeof(float);
+  const size_t o_bytes = slots * kHeads * kV * sizeof(uint16_t);
   pl->lse_offset = (o_bytes + 255) / 256 * 256;
   pl->ws_bytes = pl->lse_offset + (slots * kHeads * sizeof(float) + 255) / 256 * 256;
   *plan_out = pl;
@@ -1480,7 +1476,7 @@ mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, cons
   sp->qo_indptr = qo_indptr;
   sp->kv_indptr = kv_indptr;
   sp->out = (uint16_t*)out;
-  sp->part_o = (float*)workspace;
+  sp->part_o = (uint16_t*)workspace;
   sp->part_lse = (float*)((uint8_t*)workspace + pl->lse_offset);
   sp->total_kv = pr.total_kv;
   sp->total_q = pr.total_q;
@@ -1549,7 +1545,7 @@ mla_status mla_decode_merge(const mla_plan* pl, const int32_t* qo_indptr, const 
   if (workspace_bytes < pl->ws_bytes || (pl->ws_bytes && (!workspace || !aligned16(workspace))))
     return MLA_ERR_INVALID_ARG;
   MergeParams mp;
-  mp.part_o = (const float*)workspace;
+  mp.part_o = (const uint16_t*)workspace;
   mp.part_lse = (const float*)((const uint8_t*)workspace + pl->lse_offset);
   mp.qo_indptr = qo_indptr;
   mp.kv_indptr = kv_indptr;
