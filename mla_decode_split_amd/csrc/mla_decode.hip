@@ -1152,19 +1152,22 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p) {
   float m_run = -INFINITY, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int32_t base = g0; base <= g1; base += kMergeBatch) {
+    // straight-line loads (slots past g1 re-read slot g1 and get weight 0), so
+    // that they are all in flight before the first is used
     float lse[kMergeBatch];
-    f32x4 v[kMergeBatch];
+    uint2 u[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      lse[k] = -INFINITY;
-      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (base + k <= g1) {
-        const int64_t slot = merge_slot(base + k, g0);
-        lse[k] = p.part_lse[slot * kHeads + h];
-        const uint2 u = *(const uint2*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
-        v[k] = f32x4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
-      }
+      const int64_t slot = merge_slot(std::min(base + k, g1), g0);
+      lse[k] = p.part_lse[slot * kHeads + h];
+      u[k] = *(const uint2*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
     }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (base + k > g1) lse[k] = -INFINITY;
+    f32x4 v[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) v[k] = f32x4{bf_lo(u[k].x), bf_hi(u[k].x), bf_lo(u[k].y), bf_hi(u[k].y)};
     float mx = m_run;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) mx = fmaxf(mx, lse[k]);
