@@ -1,8 +1,8 @@
 """MLA decode benchmark on one MI355X.
 
-A step is one decode of the batch (mla_decode_split, the stage-1 split
-kernel, then mla_decode_merge, the stage-2 LSE merge - together what
-mla_decode_run launches) over seeded synthetic inputs already resident in HBM.
+A step is one decode of the batch (mla_decode_run: the stage-1 split kernel,
+then the stage-2 LSE merge) over seeded synthetic inputs already resident in
+HBM.
 The default workload is bs=64, kv_len=8192, bf16 q, fp8 E4M3FN KV (the
 bs>=32 / kv=8192 / fp8 shape the bandwidth target is stated for).  The KV
 buffer is rotated over enough copies (>= 768 MB in total) that each call reads
@@ -43,9 +43,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "7642400ce4a0cbb0540bb515cb55d44b86d7e734177cf863f76aec32ff5fb21f",
-    "fetch_kib": 152145.54,
-    "write_kib": 16493.05,
+    "source_sha256": "5fd113d2c7e9130d52f68ee982546328df72c91093713ed36f71d3ff39f16103",
+    "fetch_kib": 152173.76,
+    "write_kib": 8224.00,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
@@ -146,11 +146,11 @@ class Timed:
         self.stream = torch.cuda.current_stream()
 
     def step(self, i):
+        """One decode: mla_decode_run (stage 1, then stage 2 when the plan needs it)."""
         from mla_decode_split_amd import device as dev
 
         self.batch.kv = self.kvs[i % self.ncopy]
-        dev.run_split(self.plan, self.batch, self.out, self.ws, self.stream)
-        dev.run_merge(self.plan, self.batch, self.out, self.ws, self.stream)
+        dev.run(self.plan, self.batch, self.out, self.ws, self.stream)
 
     def time(self, steps, warmup):
         """Seconds for `steps` whole calls back to back, after `warmup` untimed ones."""
