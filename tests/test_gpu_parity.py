@@ -200,6 +200,40 @@ def test_run_on_a_side_stream():
     _compare(_bf16_out_to_f64(out), ref, "side stream")
 
 
+def test_graph_replays_match_eager():
+    """mla_decode_run captured in a HIP graph (no memset nodes: the library
+    records none) and replayed several times, with eager work and a
+    synchronisation between replays; every replay must equal the eager result
+    bit for bit, and the oracle within tolerance."""
+    w = synth.make_batch([700, 1500, 33, 4096], "bf16", "fp8", seed=909, name="graph")
+    b = dev.upload(w)
+    plan = dev.plan_for(b, rows_per_split=256)
+    ws = dev.workspace_for(plan)
+    eager = torch.empty((b.total_q, 16, 512), dtype=torch.bfloat16, device="cuda")
+    dev.run(plan, b, eager, ws)
+    torch.cuda.synchronize()
+    out = torch.full_like(eager, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dev.run(plan, b, out, ws, stream=s)  # warm the stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.run(plan, b, out, ws, stream=torch.cuda.current_stream())
+    for rep in range(4):
+        out.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda") * 2.0  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep} differs from eager"
+        del scratch
+    ref, _ = oracle.decode_workload(w, threads=8)
+    _compare(_bf16_out_to_f64(out), ref, "graph replay")
+
+
 # ------------------------------------------------------------- the five workloads
 
 SAMPLE = {
