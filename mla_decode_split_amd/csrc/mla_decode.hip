@@ -1134,20 +1134,41 @@ struct MergeParams {
 // memory after the index loads.
 constexpr int kMergeBatch = 8;
 
-__global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p) {
+// Workgroup range g0..g1 of every sequence, derived by the planner from the
+// host kv_indptr and passed with the kernel arguments (read in parallel with
+// them, where the offsets would be one more dependent load); g1 < g0 marks a
+// sequence with no rows.  Used when the plan knows the offsets, the batch
+// fits and G < 2^16.
+constexpr int kMergeTable = 512;
+struct MergeTable {
+  static constexpr bool kHas = true;
+  uint16_t g0[kMergeTable];
+  uint16_t g1[kMergeTable];
+};
+struct NoMergeTable {
+  static constexpr bool kHas = false;
+};
+
+template <typename Tab>
+__global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) {
   const int b = blockIdx.x >> 4, h = blockIdx.x & 15;
   const int t = threadIdx.x;
-  const int32_t s_raw = p.kv_indptr[b], e_raw = p.kv_indptr[b + 1], q_raw = p.qo_indptr[b];
-  const int64_t s = std::max<int64_t>(s_raw, 0);
-  const int64_t e = std::min<int64_t>(e_raw, p.total_kv);
-  const int64_t qrow = std::min(std::max(q_raw, 0), p.total_q - 1);
+  const int64_t qrow = std::min(std::max(p.qo_indptr[b], 0), p.total_q - 1);
   uint16_t* o = p.out + (qrow * kHeads + h) * kV + 4 * t;
-  if (e <= s) {  // no KV rows: the softmax is empty, the output is zero
+  int32_t g0, g1;
+  if constexpr (Tab::kHas) {
+    g0 = tab.g0[b];
+    g1 = tab.g1[b];
+  } else {
+    const int64_t s = std::max<int64_t>(p.kv_indptr[b], 0);
+    const int64_t e = std::min<int64_t>(p.kv_indptr[b + 1], p.total_kv);
+    g0 = (int32_t)std::min<int64_t>(s / p.rows_per_wg, p.num_wgs - 1);
+    g1 = e > s ? (int32_t)std::min<int64_t>((e - 1) / p.rows_per_wg, p.num_wgs - 1) : g0 - 1;
+  }
+  if (g1 < g0) {  // no KV rows: the softmax is empty, the output is zero
     *(uint2*)o = make_uint2(0u, 0u);
     return;
   }
-  const int32_t g0 = (int32_t)std::min<int64_t>(s / p.rows_per_wg, p.num_wgs - 1);
-  const int32_t g1 = (int32_t)std::min<int64_t>((e - 1) / p.rows_per_wg, p.num_wgs - 1);
   if (g0 == g1) return;  // written by stage 1
   float m_run = -INFINITY, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1252,6 +1273,8 @@ struct mla_plan {
   int32_t wgs_per_cu;
   size_t ws_bytes;
   size_t lse_offset;
+  bool has_table;  // merge ranges known at plan time (host kv_indptr, batch and G small enough)
+  MergeTable table;
 };
 
 namespace {
@@ -1386,6 +1409,17 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   const size_t slots = 2 * (size_t)G;
   const size_t o_bytes = slots * kHeads * kV * sizeof(uint16_t);
   pl->lse_offset = (o_bytes + 255) / 256 * 256;
+  pl->has_table = kv_indptr_host && pr->batch_size <= kMergeTable && G < 65536;
+  if (pl->has_table) {
+    for (int b = 0; b < pr->batch_size; ++b) {
+      const int64_t s = std::max<int64_t>(kv_indptr_host[b], 0);
+      const int64_t e = std::min<int64_t>(kv_indptr_host[b + 1], total);
+      const int64_t g0 = std::min<int64_t>(s / R, G - 1);
+      const int64_t g1 = e > s ? std::min<int64_t>((e - 1) / R, G - 1) : g0 - 1;
+      pl->table.g0[b] = (uint16_t)(g1 < g0 ? 1 : g0);  // empty: g0 = 1 > g1 = 0
+      pl->table.g1[b] = (uint16_t)(g1 < g0 ? 0 : g1);
+    }
+  }
   pl->ws_bytes = pl->lse_offset + (slots * kHeads * sizeof(float) + 255) / 256 * 256;
   *plan_out = pl;
   if (workspace_bytes) *workspace_bytes = pl->ws_bytes;
@@ -1513,7 +1547,12 @@ mla_status launch_split_stage(const mla_plan* pl, const SplitParams& sp, hipStre
 
 mla_status launch_merge_stage(const mla_plan* pl, const MergeParams& mp, hipStream_t st) {
   if (!pl->stage2) return MLA_OK;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3(pl->prob.batch_size * kHeads), dim3(128), 0, st, mp);
+  if (pl->has_table)
+    hipLaunchKernelGGL(mla_merge_kernel<MergeTable>, dim3(pl->prob.batch_size * kHeads), dim3(128), 0, st, mp,
+                       pl->table);
+  else
+    hipLaunchKernelGGL(mla_merge_kernel<NoMergeTable>, dim3(pl->prob.batch_size * kHeads), dim3(128), 0, st, mp,
+                       NoMergeTable{});
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the merge kernel");
 }
