@@ -19,20 +19,23 @@
 // 2g + (piece starts before the range ? 0 : 1), and stage 2 merges those.  This
 // balances rows, not sequences, so ragged batches keep every CU equally busy.
 //
-// Stage-1 workgroup: four wave64s (two workgroups per CU, two waves per SIMD)
-// stream the 32-row KV tiles of a piece through a shared LDS ring filled by
-// 16-byte global->LDS DMA.  Per tile, each wave:
-//   QK : S^T (32 tokens x 16 heads) = K Q^T on MFMA over all 576 dims, K from
-//        the LDS tile (A operand), Q^T held in registers (B operand); both
-//        waves compute the same scores, which costs less than exchanging them;
-//   softmax: base-2 online softmax; the head-wide max and the rescale of the
-//        accumulators run only when some score exceeds its running max;
-//   PV : O^T (the wave's 128 value columns x 16 heads) += V^T P^T, V^T
-//        gathered from the same LDS tile, P^T taken straight from the
-//        registers that hold S^T.
-// One barrier per tile publishes the tile and frees its ring slot.
-// fp8 / MXFP4 values are widened to bf16 in registers (exact); only fp8 x fp8
-// queries/keys use the fp8 matrix instruction directly.
+// Stage-1 workgroup: four wave64s (two workgroups per CU for bf16 and fp8 KV,
+// three for MXFP4; one wave of each on every SIMD) stream the 32-row KV tiles
+// of a piece through a shared LDS ring filled by 16-byte global->LDS DMA.  Per
+// tile:
+//   QK : each wave computes the partial S^T (32 tokens x 16 heads) over its
+//        quarter of the 576 dims on MFMA, K from the LDS tile (A operand, fp8
+//        and E2M1 codes fed raw to the scaled fp8/fp4 instruction), Q^T held in
+//        registers (B operand); the partials meet in LDS;
+//   softmax: each wave finishes the scores of a quarter of the tokens (base-2
+//        online softmax against a running max that is raised only when a
+//        score passes it by more than a slack) and posts the bf16
+//        probabilities into the tile's rope bytes, which no wave reads after
+//        the score exchange;
+//   PV : O^T (the wave's 128 value columns x 16 heads) += V^T P^T on bf16 MFMA,
+//        V^T gathered from the same LDS tile, P^T read back from LDS.
+// A tile costs two workgroup barriers: tile i's scores, then - after the next
+// ring barrier - tile i-1's products.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

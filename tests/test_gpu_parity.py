@@ -200,6 +200,22 @@ def test_run_on_a_side_stream():
     _compare(_bf16_out_to_f64(out), ref, "side stream")
 
 
+def test_split_then_merge_equals_run():
+    """mla_decode_split followed by mla_decode_merge on one stream gives the same
+    bits as mla_decode_run (the two stages as separate calls)."""
+    w = synth.make_batch([900, 64, 3000, 1, 2500], "bf16", "fp8", seed=1001, name="split+merge")
+    b = dev.upload(w)
+    plan = dev.plan_for(b, rows_per_split=256)
+    ws = dev.workspace_for(plan)
+    a_out = torch.full((b.total_q, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    b_out = torch.full_like(a_out, float("nan"))
+    dev.run(plan, b, a_out, ws)
+    dev.run_split(plan, b, b_out, ws)
+    dev.run_merge(plan, b, b_out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out.view(torch.int16), b_out.view(torch.int16))
+
+
 def test_graph_replays_match_eager():
     """mla_decode_run captured in a HIP graph (no memset nodes: the library
     records none) and replayed several times, with eager work and a
