@@ -54,7 +54,8 @@ typedef enum mla_dtype {
 /* The decode problem a plan is made for. */
 typedef struct mla_problem {
   int32_t batch_size; /* sequences; >= 1 */
-  int32_t total_q;    /* rows of q and out; must equal batch_size (one query token per sequence) */
+  int32_t total_q;    /* rows of q and out: batch_size when max_q_len <= 1, else in
+                         [1, batch_size * max_q_len] */
   int64_t total_kv;   /* rows in the KV buffer; kv_indptr[batch_size] <= total_kv < 2^31 */
   int32_t num_heads;  /* query heads; must be 16 */
   int32_t qk_dim;     /* key width; must be 576 (512 latent + 64 rope) */
@@ -63,14 +64,19 @@ typedef struct mla_problem {
   int32_t kv_dtype;   /* any mla_dtype; fp8 q requires fp8 KV */
   float sm_scale;     /* softmax scale, 1/sqrt(576) for DeepSeek-R1; finite and > 0 */
   int32_t num_cus;    /* compute units to plan for; 0 = ask the current HIP device */
+  int32_t max_q_len;  /* query rows per sequence at most (0 or 1: exactly one each; 2..4:
+                         qo_indptr[b+1] - qo_indptr[b] in [0, max_q_len], every row attending
+                         to all KV rows of its sequence with no mask - multi-token prediction
+                         or speculative decoding).  Larger values: MLA_ERR_UNSUPPORTED */
 } mla_problem;
 
 /* Optional planner overrides (NULL = planner's choice for every field). */
 typedef struct mla_plan_options {
   int32_t rows_per_split; /* > 0: KV rows each stage-1 workgroup takes (rounded up to 32) */
   int32_t wgs_per_cu;     /* > 0: stage-1 workgroups per CU the planner sizes the split for
-                             (default: as many as are resident together, 2 for bf16 and fp8
-                             KV, 3 for MXFP4 KV) */
+                             (default: as many as are resident together - with one query row
+                             per sequence 2 for bf16 and fp8 KV, 3 for MXFP4 KV; see
+                             mla_plan_desc.wgs_per_cu for others) */
 } mla_plan_options;
 
 /* What a plan decided (for tests, benchmarks and logs). */
@@ -79,13 +85,16 @@ typedef struct mla_plan_desc {
   int32_t rows_per_split;  /* R, a multiple of tile_rows */
   int32_t tile_rows;       /* KV rows per LDS tile */
   int32_t stages;          /* depth of the LDS tile ring */
-  int32_t partial_slots;   /* 2*G partial (O, LSE) slots in the workspace: O as bf16 [16][512]
-                              (normalised by its own running sum), LSE as fp32 [16] */
+  int32_t partial_slots;   /* 2*G partial (O, LSE) slots in the workspace, each for query_tokens
+                              rows: O as bf16 [query_tokens][16][512] (normalised by its own
+                              running sum), LSE as fp32 [query_tokens][16] */
   int32_t stage2;          /* 1 if mla_decode_run launches the LSE-merge kernel */
   int64_t workspace_bytes; /* bytes mla_decode_run needs */
   int32_t lds_bytes;       /* LDS per stage-1 workgroup */
   int32_t num_cus;         /* compute units planned for */
   int32_t wgs_per_cu;      /* stage-1 workgroups per CU the plan is sized for (resident together) */
+  int32_t query_tokens;    /* query rows of a sequence each stage-1 workgroup multiplies every KV
+                              tile with: 1, 2 or 4 (max_q_len rounded up) */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan;
@@ -122,12 +131,16 @@ mla_status mla_decode_plan(const mla_problem* problem, const mla_plan_options* o
  *              read in 16-byte units: the allocation must be readable up to the next
  *              multiple of 16 bytes past total_kv*18.
  *              bf16 KV: ignored (may be NULL).
- *   qo_indptr  device int32[batch_size + 1]; qo_indptr[b] is sequence b's query row.
+ *   qo_indptr  device int32[batch_size + 1]; sequence b's query rows are
+ *              [qo_indptr[b], qo_indptr[b+1]) - exactly one when the plan's max_q_len
+ *              is 0 or 1, else at most max_q_len (rows of a sequence with none are
+ *              not written).  Every row attends to all KV rows of its sequence.
  *   kv_indptr  device int32[batch_size + 1]; sequence b owns KV rows
  *              [kv_indptr[b], kv_indptr[b+1]).  Values inconsistent with the plan
  *              (or decreasing) give undefined output, but every access stays inside
  *              [0, total_kv) rows.
- *   out        device bf16 [total_q][16][512]; a sequence with no KV rows gets zeros.
+ *   out        device bf16 [total_q][16][512]; the rows of a sequence with no KV rows
+ *              get zeros.
  *   workspace  device scratch of at least the planned workspace_bytes (contents
  *              need not be initialised; they are overwritten).
  */

@@ -71,27 +71,22 @@ enum Dt { DT_BF16 = MLA_DTYPE_BF16, DT_FP8 = MLA_DTYPE_FP8_E4M3FN, DT_MXFP4 = ML
 // ---------------------------------------------------------------- geometry
 //
 // A tile is 32 consecutive KV rows.  The four waves of a workgroup stream the
-// tiles of a piece through a shared ring of kStages LDS slots; a slot holds the
-// tile's rows and, for MXFP4, one 1 KB chunk with the tile's E8M0 scale bytes.
-// Two (fp8, bf16) or three (MXFP4) workgroups share a CU.
+// tiles of a piece through a shared ring of LDS slots; a slot holds the tile's
+// rows and, for MXFP4, one 1 KB chunk with the tile's E8M0 scale bytes.
 
 template <int KF>
 struct KvGeom;
-// kWgsPerCu: resident workgroups per CU (one wave of each on every SIMD).  The
-// E2M1 tile is cheap to move and dear to compute, so three workgroups with
-// four-slot rings (which measured faster than two with seven); the fp8 and
-// bf16 tiles need their deeper rings to keep HBM busy, which leaves room for two.
 template <>
 struct KvGeom<DT_BF16> {
-  static constexpr int kRow = 2 * kQK, kStages = 2, kScaleChunks = 0, kDmaWaves = 4, kWgsPerCu = 2;
+  static constexpr int kRow = 2 * kQK, kScaleChunks = 0, kDmaWaves = 4;
 };
 template <>
 struct KvGeom<DT_FP8> {
-  static constexpr int kRow = kQK, kStages = 4, kScaleChunks = 0, kDmaWaves = 4, kWgsPerCu = 2;
+  static constexpr int kRow = kQK, kScaleChunks = 0, kDmaWaves = 4;
 };
 template <>
 struct KvGeom<DT_MXFP4> {
-  static constexpr int kRow = kQK / 2, kStages = 4, kScaleChunks = 1, kDmaWaves = 3, kWgsPerCu = 3;
+  static constexpr int kRow = kQK / 2, kScaleChunks = 1, kDmaWaves = 3;
 };
 
 template <int KF>
@@ -99,7 +94,6 @@ struct Geom {
   static constexpr int kRow = KvGeom<KF>::kRow;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kStages = KvGeom<KF>::kStages;
   static constexpr int kRowBytes = kTile * kRow;       // row bytes of one tile
   static constexpr int kRowChunks = kRowBytes / 1024;  // one chunk = one wave DMA instruction
   static constexpr int kChunks = kRowChunks + KvGeom<KF>::kScaleChunks;
@@ -109,15 +103,56 @@ struct Geom {
   static constexpr int kDmaWaves = KvGeom<KF>::kDmaWaves;
   static constexpr int kMaxChunksPerWave = (kChunks + kDmaWaves - 1) / kDmaWaves;
   static constexpr int kStageBytes = kChunks * 1024;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
   static_assert(kRowBytes % 1024 == 0, "a tile must fill whole DMA chunks");
-  static constexpr int kWgsPerCu = KvGeom<KF>::kWgsPerCu;
-  static_assert(kWgsPerCu * (kLdsBytes + 4 * 2 * 64 * 16 + (KF == DT_MXFP4 ? 1024 : 0)) <= 160 * 1024,
-                "resident workgroups per CU (ring + score exchange + E8M0 table)");
-  static_assert((kStages - 2) * kMaxChunksPerWave <= 63, "vmcnt range");
   __host__ __device__ static constexpr int chunks_of_wave(int w) {
     return w < kDmaWaves ? (kChunks - w + kDmaWaves - 1) / kDmaWaves : 0;
   }
+};
+
+// Partial-score exchange buffer of one query token, one plane per token of a
+// lane's f32x4: [wave][block][r][lane] floats, so the wave that finishes the
+// scores of component r reads 64 consecutive floats per (wave, block).
+constexpr int kXchgBytes = 4 * 2 * 4 * 64 * 4;
+// Probability exchange of query token t >= 1 (token 0 uses the tile's rope
+// bytes): the bf16 P of every lane (16 bytes each) and the four waves' maxima
+// of every head (16 bytes each), per tile parity.
+constexpr int kPTokBytes = 64 * 16 + kHeads * 16;
+
+// Ring depth and residency per (KV format, query tokens per sequence QL).  Each
+// query token adds its score-exchange plane, its probability buffers and ~60
+// VGPRs (query operand, accumulators, scores).
+//   QL = 1: the E2M1 tile is cheap to move and dear to compute, so three
+//     workgroups with four-slot rings (measured faster than two with seven);
+//     the fp8 and bf16 tiles need their deeper rings to keep HBM busy, which
+//     leaves room for two.
+//   QL = 2: two workgroups where the registers and LDS allow (fp8 with a
+//     three-slot ring - the same speed as four at QL = 1 - and MXFP4), one for
+//     bf16, whose 36 KB tiles leave no room for a second ring.
+//   QL = 4: one workgroup per CU with the deepest ring that fits.
+template <int KF, int QL>
+struct RingCfg;
+template <> struct RingCfg<DT_BF16, 1> { static constexpr int kStages = 2, kWgsPerCu = 2; };
+template <> struct RingCfg<DT_FP8, 1> { static constexpr int kStages = 4, kWgsPerCu = 2; };
+template <> struct RingCfg<DT_MXFP4, 1> { static constexpr int kStages = 4, kWgsPerCu = 3; };
+template <> struct RingCfg<DT_BF16, 2> { static constexpr int kStages = 3, kWgsPerCu = 1; };
+template <> struct RingCfg<DT_FP8, 2> { static constexpr int kStages = 3, kWgsPerCu = 2; };
+template <> struct RingCfg<DT_MXFP4, 2> { static constexpr int kStages = 4, kWgsPerCu = 2; };
+template <> struct RingCfg<DT_BF16, 4> { static constexpr int kStages = 3, kWgsPerCu = 1; };
+template <> struct RingCfg<DT_FP8, 4> { static constexpr int kStages = 6, kWgsPerCu = 1; };
+template <> struct RingCfg<DT_MXFP4, 4> { static constexpr int kStages = 8, kWgsPerCu = 1; };
+
+template <int KF, int QL>
+struct Ring {
+  static constexpr int kStages = RingCfg<KF, QL>::kStages;
+  static constexpr int kWgsPerCu = RingCfg<KF, QL>::kWgsPerCu;
+  static constexpr int kLdsBytes = kStages * Geom<KF>::kStageBytes;
+  static constexpr int kXchg = QL * kXchgBytes;
+  static constexpr int kPBuf = 2 * (QL - 1) * kPTokBytes;
+  static constexpr int kLut = KF == DT_MXFP4 ? 1024 : 0;  // E8M0 code -> fp32 table
+  static constexpr int kTotal = kLdsBytes + kXchg + kPBuf + kLut;
+  static_assert(kWgsPerCu * kTotal <= 160 * 1024, "resident workgroups per CU must fit the LDS");
+  static_assert((kStages - 2) * Geom<KF>::kMaxChunksPerWave <= 63, "vmcnt range");
+  static_assert(kStages >= 2 && kStages - 3 <= 5, "tiles behind the one needed near the end: 0..5");
 };
 
 // ------------------------------------------------------------ piece rules
@@ -671,36 +706,48 @@ struct QOperand {
   }
 };
 
-// This wave's partial S^T for the two 16-token blocks of a tile: s[blk][r] =
-// partial score of token 16 * blk + 4g + r for head lane & 15 (before any
-// scaling).  Two independent accumulation chains keep the matrix pipe busy.
-template <int QF, int KF>
-__device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo, int w, int m,
-                               int sdelta, f32x4 s[2]) {
-  s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  s[1] = s[0];
-  if constexpr (QOperand<QF, KF>::kByteK) {
+// This wave's partial S^T for the two 16-token blocks of a tile and each query
+// token t: s[t][blk][r] = partial score of KV row 16 * blk + 4g + r for head
+// lane & 15 of query token t (before any scaling).  The K operand is read once
+// per block and multiplied with every token's query; two independent chains
+// (the blocks) keep the matrix pipe busy.
+template <int QF, int KF, int QL>
+__device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF> (&qo)[QL], const LaneOffs<KF>& lo, int w,
+                               int m, int sdelta, f32x4 (&s)[QL][2]) {
+  using QO = QOperand<QF, KF>;
+#pragma unroll
+  for (int t = 0; t < QL; ++t) {
+    s[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[t][1] = s[t][0];
+  }
+  if constexpr (QO::kByteK) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const u32x4 k0 = *(const u32x4*)(st + lo.xw[blk][0]);
       const u32x4 k1 = *(const u32x4*)(st + lo.xw[blk][1]);
       const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
-      // formats 0/0 = fp8 E4M3 for both operands; scale exponents 127 = 2^0
-      s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.b8, s[blk], 0, 0, 0, 127, 0, 127);
-      if constexpr (QOperand<QF, KF>::kHiLo)
-        s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.l8, s[blk], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int t = 0; t < QL; ++t) {
+        // formats 0/0 = fp8 E4M3 for both operands; scale exponents 127 = 2^0
+        s[t][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo[t].b8, s[t][blk], 0, 0, 0, 127, 0, 127);
+        if constexpr (QO::kHiLo)
+          s[t][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo[t].l8, s[t][blk], 0, 0, 0, 127, 0, 127);
+      }
     }
     if (w < 2) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         // rope dims 512 + 32w + 8g + [0, 8) sit where the bf16 path's chunk 16 + w does
         const uint64_t k = *(const uint64_t*)(st + lo.kr[blk]);
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.bx, s[blk], 0, 0, 0);
-        if constexpr (QOperand<QF, KF>::kHiLo)
-          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo.lx, s[blk], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < QL; ++t) {
+          s[t][blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo[t].bx, s[t][blk], 0, 0, 0);
+          if constexpr (QO::kHiLo)
+            s[t][blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k, (long)qo[t].lx, s[t][blk], 0, 0, 0);
+        }
       }
     }
-  } else if constexpr (QOperand<QF, KF>::kFp4K) {
+  } else if constexpr (QO::kFp4K) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       // A lane group g: the 32 E2M1 codes of dims 128w + 32g + [0, 32), one E8M0
@@ -709,10 +756,13 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, co
       const u32x4 k4 = *(const u32x4*)(st + lo.xw[blk][0]);
       const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k4, u32x4{0u, 0u, 0u, 0u}, 0, 1, 2, 3, 4, 5, 6, 7));
       const int e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + 4 * w + (threadIdx.x & 63) / 16];
-      // formats: A = 4 (E2M1), B = 0 (fp8 E4M3); B scale exponent 127 = 2^0
-      s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.b8, s[blk], 4, 0, 0, e, 0, 127);
-      if constexpr (QOperand<QF, KF>::kHiLo)
-        s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo.l8, s[blk], 4, 0, 0, e, 0, 127);
+#pragma unroll
+      for (int t = 0; t < QL; ++t) {
+        // formats: A = 4 (E2M1), B = 0 (fp8 E4M3); B scale exponent 127 = 2^0
+        s[t][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo[t].b8, s[t][blk], 4, 0, 0, e, 0, 127);
+        if constexpr (QO::kHiLo)
+          s[t][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, qo[t].l8, s[t][blk], 4, 0, 0, e, 0, 127);
+      }
     }
     if (w < 2) {
 #pragma unroll
@@ -720,18 +770,22 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF>& qo, co
         // rope dims 512 + 32w + 8g + [0, 8), widened to bf16 with their block scale
         const uint32_t word = *(const uint32_t*)(st + lo.kr[blk]);
         const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + 16 + w];
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16(word, lo.e8m0[e]), qo.br, s[blk], 0, 0, 0);
+        const bf16x8 kb = fp4x8_bf16(word, lo.e8m0[e]);
+#pragma unroll
+        for (int t = 0; t < QL; ++t)
+          s[t][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qo[t].br, s[t][blk], 0, 0, 0);
       }
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < QOperand<QF, KF>::kBfChunks; ++k) {
+    for (int k = 0; k < QO::kBfChunks; ++k) {
       const int c = w + 4 * k;
-      if (k == QOperand<QF, KF>::kBfChunks - 1 && c >= kQK / 32) break;
+      if (k == QO::kBfChunks - 1 && c >= kQK / 32) break;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const bf16x8 kk = load_kw<KF>(st, lo, blk, k);
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qo.b[k], s[blk], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < QL; ++t) s[t][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qo[t].b[k], s[t][blk], 0, 0, 0);
       }
     }
   }
@@ -746,11 +800,6 @@ struct WaveState {
   float l_run;
   f32x4 acc[8];
 };
-
-// Partial-score exchange buffer, one plane per token of a lane's f32x4:
-// [wave][block][r][lane] floats, so the wave that finishes the scores of
-// component r reads 64 consecutive floats per (wave, block).
-constexpr int kXchgBytes = 4 * 2 * 4 * 64 * 4;
 
 // 16-byte units of a tile row that hold the rope dims (used only by S = Q K^T):
 // once every wave has its partial scores, the current tile's rope units carry
@@ -797,93 +846,126 @@ __device__ inline int flag_slot() {
     return Geom<KF>::kRowBytes + 704;
 }
 
+// P slot and max slot of query token t: token 0 in the tile's rope bytes, later
+// tokens in `pb`, the tile parity's kPTokBytes-sized records (t is a
+// compile-time index after unrolling, so the choice costs nothing).
+template <int KF>
+__device__ inline uint8_t* p_ptr(uint8_t* st, uint8_t* pb, int t, int lane) {
+  return t == 0 ? st + p_slot<KF>(lane) : pb + (t - 1) * kPTokBytes + 16 * lane;
+}
+template <int KF>
+__device__ inline uint8_t* max_ptr(uint8_t* st, uint8_t* pb, int t, int h) {
+  return t == 0 ? st + max_slot<KF>(h) : pb + (t - 1) * kPTokBytes + 64 * 16 + 16 * h;
+}
+
 // A tile goes through two steps, one ring barrier apart, so that every tile
 // costs two workgroup barriers and the products of consecutive tiles overlap:
 //
-// score_tile: S^T partials (this wave's share of the 576 dims) -> LDS; after
-//   the exchange barrier, the full scores of this wave's tokens 4g + w and
-//   16 + 4g + w (head m) and their probabilities relative to the running
-//   maximum -> the tile's rope bytes (no wave reads them after the exchange),
-//   with a per-wave flag: some probability would exceed 2^kRescaleSlack.
-// finish_tile (after the next barrier): when any wave flagged, the maximum is
+// score_tile: S^T partials (this wave's share of the 576 dims, every query
+//   token) -> LDS; after the exchange barrier, for each query token the full
+//   scores of this wave's KV rows 4g + w and 16 + 4g + w (head m) and their
+//   probabilities relative to the token's running maximum -> the token's P
+//   slots, with a per-wave flag word: bit t set when some probability of token
+//   t would exceed 2^kRescaleSlack.
+// finish_tile (after the next barrier): for each flagged token the maximum is
 //   raised to the tile's, the accumulators rescaled and the probabilities
 //   recomputed and exchanged again (rare: the first tile, and a score well above
-//   all before it); then every wave takes the eight probabilities its PV lanes
-//   need and multiplies them into its 128 value columns.
+//   all before it); then every wave reads V^T once and, for each token, takes
+//   the eight probabilities its PV lanes need and multiplies them into its 128
+//   value columns.
 // Below the slack bf16 P and the fp32 sums hold p = 2^(t - m_run) without loss,
 // and the final normalisation by the running sum is unchanged.
 struct TileScores {
-  float sv[2];  // raw scores of tokens 4g + w and 16 + 4g + w, head m (-inf when masked)
+  float sv[2];  // raw scores of KV rows 4g + w and 16 + 4g + w, head m (-inf when masked)
   float p[2];   // their probabilities against m_run as it was when they were posted
 };
 
-template <int QF, int KF, bool MASK>
-__device__ inline void score_tile(uint8_t* st, float* xchg, const QOperand<QF, KF>& qo, const LaneOffs<KF>& lo,
-                                  const WaveState& ws, int w, int m, int g, int sdelta, int valid, float c,
-                                  TileScores& ts) {
+template <int QF, int KF, int QL, bool MASK>
+__device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const QOperand<QF, KF> (&qo)[QL],
+                                  const LaneOffs<KF>& lo, const WaveState (&ws)[QL], int w, int m, int g, int sdelta,
+                                  int valid, const float (&c)[QL], TileScores (&ts)[QL]) {
   const int lane = threadIdx.x & 63;
   {
-    f32x4 part[2];
-    qk_tile<QF, KF>(st, qo, lo, w, m, sdelta, part);
+    f32x4 part[QL][2];
+    qk_tile<QF, KF, QL>(st, qo, lo, w, m, sdelta, part);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int t = 0; t < QL; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xchg[((2 * w + blk) * 4 + r) * 64 + lane] = part[blk][r];
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xchg[t * (kXchgBytes / 4) + ((2 * w + blk) * 4 + r) * 64 + lane] = part[t][blk][r];
   }
   lds_barrier();  // every wave's partial scores are in LDS and every wave is done with the rope dims
+  int flags = 0;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    // summed in wave order
-    float t = xchg[((0 + blk) * 4 + w) * 64 + lane];
-    t += xchg[((2 + blk) * 4 + w) * 64 + lane];
-    t += xchg[((4 + blk) * 4 + w) * 64 + lane];
-    t += xchg[((6 + blk) * 4 + w) * 64 + lane];
-    ts.sv[blk] = (MASK && 16 * blk + 4 * g + w >= valid) ? -INFINITY : t;
+  for (int t = 0; t < QL; ++t) {
+    const float* xt = xchg + t * (kXchgBytes / 4);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      // summed in wave order
+      float v = xt[((0 + blk) * 4 + w) * 64 + lane];
+      v += xt[((2 + blk) * 4 + w) * 64 + lane];
+      v += xt[((4 + blk) * 4 + w) * 64 + lane];
+      v += xt[((6 + blk) * 4 + w) * 64 + lane];
+      ts[t].sv[blk] = (MASK && 16 * blk + 4 * g + w >= valid) ? -INFINITY : v;
+    }
+    // the base-2 score is sv * c with c > 0
+    const float t0 = fmaf(ts[t].sv[0], c[t], -ws[t].m_run), t1 = fmaf(ts[t].sv[1], c[t], -ws[t].m_run);
+    ts[t].p[0] = __builtin_amdgcn_exp2f(t0);
+    ts[t].p[1] = __builtin_amdgcn_exp2f(t1);
+    uint8_t* ps = p_ptr<KF>(st, pb, t, lane);
+    *(__bf16*)(ps + 2 * w) = (__bf16)ts[t].p[0];
+    *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts[t].p[1];
+    if (__builtin_amdgcn_ballot_w64(t0 > kRescaleSlack || t1 > kRescaleSlack) != 0) flags |= 1 << t;
   }
-  // the base-2 score is sv * c with c > 0
-  const float t0 = fmaf(ts.sv[0], c, -ws.m_run), t1 = fmaf(ts.sv[1], c, -ws.m_run);
-  ts.p[0] = __builtin_amdgcn_exp2f(t0);
-  ts.p[1] = __builtin_amdgcn_exp2f(t1);
-  uint8_t* ps = st + p_slot<KF>(lane);
-  *(__bf16*)(ps + 2 * w) = (__bf16)ts.p[0];
-  *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts.p[1];
-  const bool big = __builtin_amdgcn_ballot_w64(t0 > kRescaleSlack || t1 > kRescaleSlack) != 0;
-  if (lane == 0) ((int*)(st + flag_slot<KF>()))[w] = big ? 1 : 0;
+  if (lane == 0) ((int*)(st + flag_slot<KF>()))[w] = flags;
 }
 
-template <int QF, int KF, bool MASK>
-__device__ inline void finish_tile(uint8_t* st, const LaneOffs<KF>& lo, WaveState& ws, int w, int m, int g,
-                                   int sdelta, int valid, float c, TileScores& ts) {
+template <int QF, int KF, int QL, bool MASK>
+__device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>& lo, WaveState (&ws)[QL], int w, int m,
+                                   int g, int sdelta, int valid, const float (&c)[QL], TileScores (&ts)[QL]) {
   const int lane = threadIdx.x & 63;
-  uint8_t* ps = st + p_slot<KF>(lane);
   bf16x8 va[8];
   load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
   const u32x4 fl = *(const u32x4*)(st + flag_slot<KF>());
-  if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0u) {
-    // tile maximum per head: this wave's tokens (over the lane groups), then the waves
-    float mx = fmaxf(ts.sv[0], ts.sv[1]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    if (g == 0) *(float*)(st + max_slot<KF>(m) + 4 * w) = mx * c;
+  const uint32_t any = fl[0] | fl[1] | fl[2] | fl[3];
+  if (any != 0u) {
+#pragma unroll
+    for (int t = 0; t < QL; ++t) {
+      if (!((any >> t) & 1u)) continue;
+      // tile maximum per head: this wave's rows (over the lane groups), then the waves
+      float mx = fmaxf(ts[t].sv[0], ts[t].sv[1]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      if (g == 0) *(float*)(max_ptr<KF>(st, pb, t, m) + 4 * w) = mx * c[t];
+    }
     lds_barrier();
-    const f32x4 mw = *(const f32x4*)(st + max_slot<KF>(m));
-    const float tmax = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-    const float m_new = fmaxf(ws.m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
-    ws.m_run = m_new;
-    ws.l_run *= alpha;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ws.acc[j] *= alpha;
-    ts.p[0] = __builtin_amdgcn_exp2f(fmaf(ts.sv[0], c, -ws.m_run));
-    ts.p[1] = __builtin_amdgcn_exp2f(fmaf(ts.sv[1], c, -ws.m_run));
-    *(__bf16*)(ps + 2 * w) = (__bf16)ts.p[0];
-    *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts.p[1];
-    lds_barrier();  // the probabilities against the new maximum are in LDS
+    for (int t = 0; t < QL; ++t) {
+      if (!((any >> t) & 1u)) continue;
+      const f32x4 mw = *(const f32x4*)max_ptr<KF>(st, pb, t, m);
+      const float tmax = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+      const float m_new = fmaxf(ws[t].m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(ws[t].m_run - m_new);
+      ws[t].m_run = m_new;
+      ws[t].l_run *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ws[t].acc[j] *= alpha;
+      ts[t].p[0] = __builtin_amdgcn_exp2f(fmaf(ts[t].sv[0], c[t], -ws[t].m_run));
+      ts[t].p[1] = __builtin_amdgcn_exp2f(fmaf(ts[t].sv[1], c[t], -ws[t].m_run));
+      uint8_t* ps = p_ptr<KF>(st, pb, t, lane);
+      *(__bf16*)(ps + 2 * w) = (__bf16)ts[t].p[0];
+      *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts[t].p[1];
+    }
+    lds_barrier();  // the probabilities against the new maxima are in LDS
   }
-  ws.l_run += ts.p[0] + ts.p[1];
-  const bf16x8 pb = __builtin_bit_cast(bf16x8, *(const u32x4*)ps);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ws.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, ws.acc[j], 0, 0, 0);
+  for (int t = 0; t < QL; ++t) {
+    ws[t].l_run += ts[t].p[0] + ts[t].p[1];
+    const bf16x8 pv = __builtin_bit_cast(bf16x8, *(const u32x4*)p_ptr<KF>(st, pb, t, lane));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ws[t].acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pv, ws[t].acc[j], 0, 0, 0);
+  }
 }
 
 // Workgroups share each CU, and the SIMD arbiter favours older waves, so with
@@ -900,12 +982,15 @@ __device__ inline void set_priority(int prio) {
   }
 }
 
-template <int QF, int KF>
-__device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg,
-                            const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow, int64_t r0, int n, int32_t slot,
-                            float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
+// One piece: rows [r0, r0 + n) of a sequence whose query rows are qrow0 ..
+// qrow0 + nq - 1 (nq in [1, QL]; the operands of tokens past nq repeat the
+// last row and their results are dropped).
+template <int QF, int KF, int QL>
+__device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf,
+                            const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow0, int nq, int64_t r0,
+                            int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
   using G = Geom<KF>;
-  constexpr int NS = G::kStages;
+  constexpr int NS = Ring<KF, QL>::kStages;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -952,19 +1037,27 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg,
   lo.init(m, g, w);
   lo.e8m0 = e8m0_lut;
 
-  QOperand<QF, KF> qop;
-  qop.fetch(p.q, qrow, lane, w);
-  qop.arrive();
+  QOperand<QF, KF> qop[QL];
+#pragma unroll
+  for (int t = 0; t < QL; ++t) qop[t].fetch(p.q, qrow0 + std::min(t, nq - 1), lane, w);
+#pragma unroll
+  for (int t = 0; t < QL; ++t) qop[t].arrive();
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
-  qop.prepare(xchg + 256, w, lane);  // clear of the sequence counts at the start of xchg
-  qop.settle();
-
-  WaveState ws;
-  ws.m_run = -INFINITY;
-  ws.l_run = 0.f;
+  // per-token head maxima past the sequence counts at the start of xchg
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ws.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < QL; ++t) qop[t].prepare(xchg + 256 + 64 * t, w, lane);
+#pragma unroll
+  for (int t = 0; t < QL; ++t) qop[t].settle();
+
+  WaveState ws[QL];
+#pragma unroll
+  for (int t = 0; t < QL; ++t) {
+    ws[t].m_run = -INFINITY;
+    ws[t].l_run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ws[t].acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int my_chunks = G::chunks_of_wave(w);
   // tile i is complete in LDS and every wave is done with tile i - 1
@@ -1003,68 +1096,86 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg,
       set_priority(prio);
     }
   };
-  const float c = score_scale * qop.scale;
+  float cs[QL];
+#pragma unroll
+  for (int t = 0; t < QL; ++t) cs[t] = score_scale * qop[t].scale;
   const int last_valid = n - (ntiles - 1) * kTile;
   auto stage = [&](int i) { return ring + (i % NS) * G::kStageBytes; };
-  TileScores ts;
+  // probability records of tokens >= 1: one set per tile parity
+  auto pbuf_of = [&](int i) { return pbuf + (i & 1) * ((QL - 1) * kPTokBytes); };
+  TileScores ts[QL];
   // tile 0, then for each later tile: its scores and the previous tile's products
   priority(0);
   advance(0);
   if (nfull > 0)
-    score_tile<QF, KF, false>(stage(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), kTile, c, ts);
+    score_tile<QF, KF, QL, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), kTile, cs, ts);
   else
-    score_tile<QF, KF, true>(stage(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), last_valid, c, ts);
+    score_tile<QF, KF, QL, true>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), last_valid, cs, ts);
   refill(0);
   for (int i = 1; i < nfull; ++i) {
     priority(i);
     advance(i);
-    finish_tile<QF, KF, false>(stage(i - 1), lo, ws, w, m, g, sdelta_of(i - 1), kTile, c, ts);
-    score_tile<QF, KF, false>(stage(i), xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile, c, ts);
+    finish_tile<QF, KF, QL, false>(stage(i - 1), pbuf_of(i - 1), lo, ws, w, m, g, sdelta_of(i - 1), kTile, cs, ts);
+    score_tile<QF, KF, QL, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile, cs, ts);
     refill(i);
   }
   if (nfull > 0 && nfull < ntiles) {  // the partial last tile
     advance(nfull);
-    finish_tile<QF, KF, false>(stage(nfull - 1), lo, ws, w, m, g, sdelta_of(nfull - 1), kTile, c, ts);
-    score_tile<QF, KF, true>(stage(nfull), xchg, qop, lo, ws, w, m, g, sdelta_of(nfull), last_valid, c, ts);
+    finish_tile<QF, KF, QL, false>(stage(nfull - 1), pbuf_of(nfull - 1), lo, ws, w, m, g, sdelta_of(nfull - 1), kTile,
+                                   cs, ts);
+    score_tile<QF, KF, QL, true>(stage(nfull), pbuf_of(nfull), xchg, qop, lo, ws, w, m, g, sdelta_of(nfull),
+                                 last_valid, cs, ts);
   }
   lds_barrier();  // the last tile's probabilities are in LDS
   if (nfull < ntiles)
-    finish_tile<QF, KF, true>(stage(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1), last_valid, c, ts);
+    finish_tile<QF, KF, QL, true>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1),
+                                  last_valid, cs, ts);
   else
-    finish_tile<QF, KF, false>(stage(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1), kTile, c, ts);
+    finish_tile<QF, KF, QL, false>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1),
+                                   kTile, cs, ts);
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
-  // running sum: this wave's tokens (over the lane groups), then over the waves
+  // running sums: this wave's rows (over the lane groups), then over the waves
   // (every wave is past its last read of the score planes)
-  float lt = ws.l_run + shfl_xor(ws.l_run, 16);
-  lt += shfl_xor(lt, 32);
-  if (g == 0) xchg[16 * w + m] = lt;
+  float lt[QL];
+#pragma unroll
+  for (int t = 0; t < QL; ++t) {
+    lt[t] = ws[t].l_run + shfl_xor(ws[t].l_run, 16);
+    lt[t] += shfl_xor(lt[t], 32);
+    if (g == 0) xchg[64 * t + 16 * w + m] = lt[t];
+  }
   lds_barrier();
-  lt = xchg[m] + xchg[16 + m] + xchg[32 + m] + xchg[48 + m];
-  const float inv = out_scale / lt;
   const int col0 = 128 * w + 32 * g;
-  {
+#pragma unroll
+  for (int t = 0; t < QL; ++t) {
+    if (t >= nq) break;
+    lt[t] = xchg[64 * t + m] + xchg[64 * t + 16 + m] + xchg[64 * t + 32 + m] + xchg[64 * t + 48 + m];
+    const float inv = out_scale / lt[t];
     // whole sequence: the output; piece of a split one: its partial O, also bf16 (the
     // merge adds at most one bf16 rounding of the weighted terms to the output's own)
-    uint16_t* o = (slot < 0 ? p.out + (qrow * kHeads + m) * kV : p.part_o + ((int64_t)slot * kHeads + m) * kV) + col0;
+    uint16_t* o = (slot < 0 ? p.out + ((qrow0 + t) * kHeads + m) * kV
+                            : p.part_o + (((int64_t)slot * QL + t) * kHeads + m) * kV) +
+                  col0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       u32x4 v;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = pack_bf16x2(ws.acc[2 * k][r] * inv, ws.acc[2 * k + 1][r] * inv);
+      for (int k = 0; k < 4; ++k) v[k] = pack_bf16x2(ws[t].acc[2 * k][r] * inv, ws[t].acc[2 * k + 1][r] * inv);
       *(u32x4*)(o + 8 * r) = v;
     }
+    if (slot >= 0 && w == 0 && g == 0)
+      p.part_lse[((int64_t)slot * QL + t) * kHeads + m] = (ws[t].m_run + __builtin_amdgcn_logf(lt[t])) * kLn2;
   }
-  if (slot >= 0 && w == 0 && g == 0)
-    p.part_lse[(int64_t)slot * kHeads + m] = (ws.m_run + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
-template <int QF, int KF>
-__global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(Geom<KF>::kWgsPerCu, Geom<KF>::kWgsPerCu))) void mla_split_kernel(
-    SplitParams p) {
+template <int QF, int KF, int QL>
+__global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(
+    Ring<KF, QL>::kWgsPerCu, Ring<KF, QL>::kWgsPerCu))) void mla_split_kernel(SplitParams p) {
   using G = Geom<KF>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[G::kLdsBytes];
-  __shared__ float xchg[kXchgBytes / 4];
+  using RG = Ring<KF, QL>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kLdsBytes];
+  __shared__ float xchg[RG::kXchg / 4];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[QL > 1 ? RG::kPBuf : 16];
   __shared__ float e8m0_lut[KF == DT_MXFP4 ? 256 : 1];
   int* counts = (int*)xchg;  // the sequence search runs before any exchange
 
@@ -1103,15 +1214,25 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
   const float out_scale = ks;
 
   for (int b = b_first; b < b_end; ++b) {
-    // the three loads are independent; issue them together
+    // the loads are independent; issue them together
     const int32_t s_raw = p.kv_indptr[b], e_raw = p.kv_indptr[b + 1], q_raw = p.qo_indptr[b];
+    int32_t qe_raw = 0;
+    if constexpr (QL > 1) qe_raw = p.qo_indptr[b + 1];
     const int64_t s = uniform(s_raw);
     const int64_t e = uniform(e_raw);
-    const int64_t qrow = std::min(std::max(uniform(q_raw), 0), p.total_q - 1);
+    const int64_t qrow0 = std::min(std::max(uniform(q_raw), 0), p.total_q - 1);
+    int nq = 1;
+    if constexpr (QL > 1) {
+      // query rows of the sequence, at most QL and inside the q buffer
+      nq = (int)std::min<int64_t>(std::min<int64_t>(std::max<int64_t>((int64_t)uniform(qe_raw) - uniform(q_raw), 0), QL),
+                                  p.total_q - qrow0);
+      if (nq <= 0) continue;
+    }
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
-    split_piece<QF, KF>(p, ring, xchg, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow, r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
+    split_piece<QF, KF, QL>(p, ring, xchg, pbuf, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
+                            r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
     lds_barrier();  // the next piece refills the ring
   }
 }
@@ -1130,11 +1251,12 @@ struct MergeParams {
   int32_t num_wgs;
 };
 
-// One workgroup of 128 threads per (sequence, head); thread t owns columns
-// 4t..4t+3.  The log-sum-exps and partial outputs of up to kMergeBatch slots
-// are loaded together (none depends on another), then combined with a running
-// maximum, so a sequence of up to kMergeBatch pieces costs one round trip to
-// memory after the index loads.
+// One workgroup of 128 threads per (sequence, query token, head); thread i owns
+// columns 4i..4i+3.  The log-sum-exps and partial outputs of up to kMergeBatch
+// slots are loaded together (none depends on another), then combined with a
+// running maximum, so a sequence of up to kMergeBatch pieces costs one round
+// trip to memory after the index loads.  Partial slot s holds QL query tokens:
+// O at ((s * QL + t) * 16 + h) * 512, LSE at (s * QL + t) * 16 + h.
 constexpr int kMergeBatch = 8;
 
 // Workgroup range g0..g1 of every sequence, derived by the planner from the
@@ -1152,11 +1274,20 @@ struct NoMergeTable {
   static constexpr bool kHas = false;
 };
 
-template <typename Tab>
+template <typename Tab, int QL>
 __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) {
-  const int b = blockIdx.x >> 4, h = blockIdx.x & 15;
+  const int bt = blockIdx.x >> 4, h = blockIdx.x & 15;
+  const int b = bt / QL, tq = bt % QL;
   const int t = threadIdx.x;
-  const int64_t qrow = std::min(std::max(p.qo_indptr[b], 0), p.total_q - 1);
+  int64_t qrow;
+  if constexpr (QL == 1) {
+    qrow = std::min(std::max(p.qo_indptr[b], 0), p.total_q - 1);
+  } else {
+    const int32_t q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
+    qrow = (int64_t)q0 + tq;
+    // the same query rows stage 1 takes: at most QL, inside the q buffer
+    if (tq >= (int64_t)q1 - q0 || q0 < 0 || qrow >= p.total_q) return;
+  }
   uint16_t* o = p.out + (qrow * kHeads + h) * kV + 4 * t;
   int32_t g0, g1;
   if constexpr (Tab::kHas) {
@@ -1182,7 +1313,7 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     uint2 u[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int64_t slot = merge_slot(std::min(base + k, g1), g0);
+      const int64_t slot = (int64_t)merge_slot(std::min(base + k, g1), g0) * QL + tq;
       lse[k] = p.part_lse[slot * kHeads + h];
       u[k] = *(const uint2*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
     }
@@ -1274,6 +1405,7 @@ struct mla_plan {
   int32_t stage2;
   int32_t num_cus;
   int32_t wgs_per_cu;
+  int32_t ql;  // query tokens per sequence a stage-1 workgroup holds (1, 2 or 4)
   size_t ws_bytes;
   size_t lse_offset;
   bool has_table;  // merge ranges known at plan time (host kv_indptr, batch and G small enough)
@@ -1289,28 +1421,26 @@ mla_status hip_fail(hipError_t e, const char* what) {
   return MLA_ERR_HIP;
 }
 
-int tile_stages(int kv_dtype) {
+struct RingInfo {
+  int stages, lds_bytes, wgs_per_cu;
+};
+
+template <int KF, int QL>
+constexpr RingInfo ring_info() {
+  return RingInfo{Ring<KF, QL>::kStages, Ring<KF, QL>::kTotal, Ring<KF, QL>::kWgsPerCu};
+}
+
+template <int QL>
+RingInfo ring_info_for(int kv_dtype) {
   switch (kv_dtype) {
-    case DT_BF16: return Geom<DT_BF16>::kStages;
-    case DT_FP8: return Geom<DT_FP8>::kStages;
-    default: return Geom<DT_MXFP4>::kStages;
+    case DT_BF16: return ring_info<DT_BF16, QL>();
+    case DT_FP8: return ring_info<DT_FP8, QL>();
+    default: return ring_info<DT_MXFP4, QL>();
   }
 }
 
-int lds_bytes_for(int kv_dtype) {
-  switch (kv_dtype) {
-    case DT_BF16: return Geom<DT_BF16>::kLdsBytes + kXchgBytes;
-    case DT_FP8: return Geom<DT_FP8>::kLdsBytes + kXchgBytes;
-    default: return Geom<DT_MXFP4>::kLdsBytes + kXchgBytes + 256 * 4;  // + the E8M0 table
-  }
-}
-
-int wgs_per_cu_for(int kv_dtype) {
-  switch (kv_dtype) {
-    case DT_BF16: return Geom<DT_BF16>::kWgsPerCu;
-    case DT_FP8: return Geom<DT_FP8>::kWgsPerCu;
-    default: return Geom<DT_MXFP4>::kWgsPerCu;
-  }
+RingInfo ring_info_for(int kv_dtype, int ql) {
+  return ql == 1 ? ring_info_for<1>(kv_dtype) : ql == 2 ? ring_info_for<2>(kv_dtype) : ring_info_for<4>(kv_dtype);
 }
 
 // Smallest row range worth a workgroup: below it the partial write-back and the
@@ -1327,7 +1457,13 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 template <int QF, int KF>
 hipError_t launch_split(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
-  hipLaunchKernelGGL((mla_split_kernel<QF, KF>), dim3(pl->num_wgs), dim3(Geom<KF>::kThreads), 0, st, sp);
+  const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads);
+  if (pl->ql == 1)
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1>), grid, block, 0, st, sp);
+  else if (pl->ql == 2)
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2>), grid, block, 0, st, sp);
+  else
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4>), grid, block, 0, st, sp);
   return hipGetLastError();
 }
 
@@ -1357,7 +1493,12 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
       !(pr->sm_scale < INFINITY))
     return MLA_ERR_INVALID_ARG;
   if (pr->num_heads != kHeads || pr->qk_dim != kQK || pr->v_dim != kV) return MLA_ERR_UNSUPPORTED;
-  if (pr->total_q != pr->batch_size) return MLA_ERR_UNSUPPORTED;  // one query token per sequence
+  // query rows per sequence: one, or up to max_q_len (2 or 4 kernels; 3 runs on the 4-token one)
+  if (pr->max_q_len < 0 || pr->max_q_len > 4) return MLA_ERR_UNSUPPORTED;
+  const int ql = pr->max_q_len <= 1 ? 1 : pr->max_q_len == 2 ? 2 : 4;
+  if (ql == 1 && pr->total_q != pr->batch_size) return MLA_ERR_UNSUPPORTED;  // one query token per sequence
+  if (ql > 1 && (pr->total_q < 1 || (int64_t)pr->total_q > (int64_t)pr->batch_size * pr->max_q_len))
+    return MLA_ERR_INVALID_ARG;
   if (pr->q_dtype != DT_BF16 && pr->q_dtype != DT_FP8) return MLA_ERR_UNSUPPORTED;
   if (pr->kv_dtype != DT_BF16 && pr->kv_dtype != DT_FP8 && pr->kv_dtype != DT_MXFP4) return MLA_ERR_UNSUPPORTED;
   if (opt && (opt->rows_per_split < 0 || opt->wgs_per_cu < 0)) return MLA_ERR_INVALID_ARG;
@@ -1377,7 +1518,8 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   }
 
   const int64_t total = pr->total_kv;
-  const int wpc = (opt && opt->wgs_per_cu > 0) ? opt->wgs_per_cu : wgs_per_cu_for(pr->kv_dtype);
+  const RingInfo ri = ring_info_for(pr->kv_dtype, ql);
+  const int wpc = (opt && opt->wgs_per_cu > 0) ? opt->wgs_per_cu : ri.wgs_per_cu;
   int64_t R;
   if (opt && opt->rows_per_split > 0) {
     R = opt->rows_per_split;
@@ -1404,13 +1546,14 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   pl->prob.num_cus = num_cus;
   pl->rows_per_wg = (int32_t)R;
   pl->num_wgs = (int32_t)G;
-  pl->stages = tile_stages(pr->kv_dtype);
-  pl->lds_bytes = lds_bytes_for(pr->kv_dtype);
+  pl->stages = ri.stages;
+  pl->lds_bytes = ri.lds_bytes;
+  pl->ql = ql;
   pl->stage2 = stage2 ? 1 : 0;
   pl->num_cus = num_cus;
   pl->wgs_per_cu = wpc;
   const size_t slots = 2 * (size_t)G;
-  const size_t o_bytes = slots * kHeads * kV * sizeof(uint16_t);
+  const size_t o_bytes = slots * ql * kHeads * kV * sizeof(uint16_t);
   pl->lse_offset = (o_bytes + 255) / 256 * 256;
   pl->has_table = kv_indptr_host && pr->batch_size <= kMergeTable && G < 65536;
   if (pl->has_table) {
@@ -1423,7 +1566,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
       pl->table.g1[b] = (uint16_t)(g1 < g0 ? 0 : g1);
     }
   }
-  pl->ws_bytes = pl->lse_offset + (slots * kHeads * sizeof(float) + 255) / 256 * 256;
+  pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
   *plan_out = pl;
   if (workspace_bytes) *workspace_bytes = pl->ws_bytes;
   return MLA_OK;
@@ -1443,6 +1586,7 @@ mla_status mla_decode_plan_describe(const mla_plan* pl, mla_plan_desc* d) {
   d->lds_bytes = pl->lds_bytes;
   d->num_cus = pl->num_cus;
   d->wgs_per_cu = pl->wgs_per_cu;
+  d->query_tokens = pl->ql;
   return MLA_OK;
 }
 
@@ -1550,12 +1694,22 @@ mla_status launch_split_stage(const mla_plan* pl, const SplitParams& sp, hipStre
 
 mla_status launch_merge_stage(const mla_plan* pl, const MergeParams& mp, hipStream_t st) {
   if (!pl->stage2) return MLA_OK;
-  if (pl->has_table)
-    hipLaunchKernelGGL(mla_merge_kernel<MergeTable>, dim3(pl->prob.batch_size * kHeads), dim3(128), 0, st, mp,
-                       pl->table);
-  else
-    hipLaunchKernelGGL(mla_merge_kernel<NoMergeTable>, dim3(pl->prob.batch_size * kHeads), dim3(128), 0, st, mp,
-                       NoMergeTable{});
+  const dim3 grid(pl->prob.batch_size * pl->ql * kHeads), block(128);
+  if (pl->has_table) {
+    if (pl->ql == 1)
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 1>), grid, block, 0, st, mp, pl->table);
+    else if (pl->ql == 2)
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 2>), grid, block, 0, st, mp, pl->table);
+    else
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 4>), grid, block, 0, st, mp, pl->table);
+  } else {
+    if (pl->ql == 1)
+      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 1>), grid, block, 0, st, mp, NoMergeTable{});
+    else if (pl->ql == 2)
+      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 2>), grid, block, 0, st, mp, NoMergeTable{});
+    else
+      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 4>), grid, block, 0, st, mp, NoMergeTable{});
+  }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the merge kernel");
 }

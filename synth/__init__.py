@@ -199,8 +199,10 @@ class Workload:
 
 
 def make_batch(lengths, q_dtype: str, kv_dtype: str, seed: int, name: str = "custom",
-               threads: int | None = None) -> Workload:
-    """Build a decode batch with q_len = 1 per sequence and the given KV lengths.
+               threads: int | None = None, q_lens=None) -> Workload:
+    """Build a decode batch with the given KV lengths and query rows per
+    sequence (``q_lens``, default one each; sequence b's rows are
+    qo_indptr[b] .. qo_indptr[b+1] - 1).
 
     Every tensor starts from bf16 N(0,1) draws of its own stream; fp8 tensors
     are quantised per tensor (amax / 448) and MXFP4 per 32-element block."""
@@ -208,15 +210,23 @@ def make_batch(lengths, q_dtype: str, kv_dtype: str, seed: int, name: str = "cus
     bs = int(lengths.shape[0])
     kv_indptr = np.zeros(bs + 1, dtype=np.int32)
     kv_indptr[1:] = np.cumsum(lengths).astype(np.int32)
-    qo_indptr = np.arange(bs + 1, dtype=np.int32)
+    if q_lens is None:
+        qo_indptr = np.arange(bs + 1, dtype=np.int32)
+    else:
+        q_lens = np.asarray(q_lens, dtype=np.int64)
+        if q_lens.shape != (bs,) or (q_lens < 0).any():
+            raise ValueError("q_lens: one non-negative count per sequence")
+        qo_indptr = np.zeros(bs + 1, dtype=np.int32)
+        qo_indptr[1:] = np.cumsum(q_lens).astype(np.int32)
+    total_q = int(qo_indptr[-1])
     total_kv = int(kv_indptr[-1])
-    nq = bs * NUM_HEADS * QK_DIM
+    nq = total_q * NUM_HEADS * QK_DIM
     q_scale = None
     if q_dtype == "bf16":
-        q = normal_bf16(seed, STREAM_Q, nq, threads).reshape(bs, NUM_HEADS, QK_DIM)
+        q = normal_bf16(seed, STREAM_Q, nq, threads).reshape(total_q, NUM_HEADS, QK_DIM)
     elif q_dtype == "fp8":
         qc, q_scale = fp8_tensor(seed, STREAM_Q, nq, threads)
-        q = qc.reshape(bs, NUM_HEADS, QK_DIM)
+        q = qc.reshape(total_q, NUM_HEADS, QK_DIM)
     else:
         raise ValueError(q_dtype)
     if kv_dtype == "bf16":
@@ -231,7 +241,7 @@ def make_batch(lengths, q_dtype: str, kv_dtype: str, seed: int, name: str = "cus
         raise ValueError(kv_dtype)
     return Workload(name=name, q_dtype=q_dtype, kv_dtype=kv_dtype, q=q, q_scale=q_scale, kv=kv,
                     kv_scale=kv_scale, qo_indptr=qo_indptr, kv_indptr=kv_indptr,
-                    meta={"seed": seed, "lengths": lengths})
+                    meta={"seed": seed, "lengths": lengths, "q_lens": np.diff(qo_indptr)})
 
 
 # The five decode workloads: (batch size, KV length or "ragged", q dtype, KV dtype, seed).

@@ -150,6 +150,35 @@ def _status(fn, *args):
     return mla.MLA_OK
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("max_q_len,tokens", [(0, 1), (1, 1), (2, 2), (3, 4), (4, 4)])
+def test_plans_with_several_query_rows(kv_dtype, max_q_len, tokens):
+    ind = _indptr([8192] * 64)
+    total_q = 64 * max(max_q_len, 1)
+    prob = mla.make_problem(64, int(ind[-1]), "bf16", kv_dtype, total_q=total_q, num_cus=256, max_q_len=max_q_len)
+    plan = mla.mla_decode_plan(prob, None, ind)
+    d = mla.mla_decode_plan_describe(plan)
+    assert d["query_tokens"] == tokens
+    assert d["lds_bytes"] * d["wgs_per_cu"] <= 160 * 1024
+    if tokens == 1:
+        assert d["wgs_per_cu"] == (3 if kv_dtype == "mxfp4" else 2)
+    # every partial slot holds O and LSE of each of the workgroup's query tokens
+    assert plan.workspace_bytes >= d["partial_slots"] * tokens * 16 * (512 * 2 + 4)
+    _check_cut(plan, ind)
+
+
+def test_several_query_rows_argument_errors():
+    for bad_len in (5, 8, -1):
+        prob = mla.make_problem(4, 100, total_q=4, num_cus=256, max_q_len=bad_len)
+        assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_UNSUPPORTED, bad_len
+    # more query rows than batch_size * max_q_len, or none at all
+    for total_q in (9, 0):
+        prob = mla.make_problem(4, 100, total_q=total_q, num_cus=256, max_q_len=2)
+        assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG, total_q
+    prob = mla.make_problem(4, 100, total_q=3, num_cus=256, max_q_len=2)  # some sequences with one row
+    assert _status(mla.mla_decode_plan, prob) == mla.MLA_OK
+
+
 def test_plan_argument_errors():
     unsupported = [
         dict(num_heads=8), dict(qk_dim=512), dict(v_dim=576), dict(total_q=8),

@@ -62,8 +62,15 @@ def _check_batch(w, rows_per_split=0, seq_ids=None, use_host_indptr=True, poison
     got = _bf16_out_to_f64(out)
     ref, _ = oracle.decode_workload(w, seq_ids=seq_ids, threads=8)
     if seq_ids is not None:
-        got, ref = got[seq_ids], ref[seq_ids]
+        rows = _query_rows(w, seq_ids)
+        got, ref = got[rows], ref[rows]
     return _compare(got, ref, what or w.name), plan, out
+
+
+def _query_rows(w, seq_ids):
+    """Output rows of the given sequences (several per sequence when q_len > 1)."""
+    qo = np.asarray(w.qo_indptr, dtype=np.int64)
+    return np.concatenate([np.arange(qo[b], qo[b + 1]) for b in seq_ids]).astype(np.int64)
 
 
 # ------------------------------------------------------------- dequantisation
@@ -175,6 +182,56 @@ def test_unaligned_mxfp4_scale_rows():
         _check_batch(w, rows_per_split=rows, what=f"mxfp4 unaligned starts rows={rows}")
 
 
+# ------------------------------------------------------------- several query rows per sequence
+
+@pytest.mark.parametrize("q_len", [2, 3, 4])
+@pytest.mark.parametrize("q_dtype,kv_dtype", COMBOS)
+def test_multi_token_edge_lengths(q_dtype, kv_dtype, q_len):
+    # every sequence has q_len query rows (multi-token prediction / speculative decoding)
+    w = synth.make_batch(EDGE_LENGTHS, q_dtype, kv_dtype, seed=111 + q_len, name="mtp-edges",
+                         q_lens=[q_len] * len(EDGE_LENGTHS))
+    (_, _), plan, _ = _check_batch(w, what=f"q_len {q_len} edge lengths {q_dtype}/{kv_dtype}")
+    assert mla.mla_decode_plan_describe(plan)["query_tokens"] == (4 if q_len == 3 else q_len)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("rows", [32, 96, 512])
+def test_multi_token_ragged_rows_and_splits(kv_dtype, rows):
+    # query rows 0..4 per sequence, KV lengths from 0 up, pieces of 1 to many tiles
+    lengths = [700, 0, 33, 1000, 1, 257, 64, 0]
+    q_lens = [2, 3, 4, 1, 0, 4, 3, 2]
+    w = synth.make_batch(lengths, "bf16", kv_dtype, seed=222, name="mtp-ragged", q_lens=q_lens)
+    (_, _), _, out = _check_batch(w, rows_per_split=rows, what=f"ragged q rows, rows_per_split={rows} kv={kv_dtype}")
+    qo = w.qo_indptr
+    o = out.float().cpu().numpy()
+    for b in (1, 7):  # no KV rows: zeros
+        assert np.all(o[qo[b]:qo[b + 1]] == 0.0)
+
+
+def test_multi_token_plan_without_host_indptr():
+    w = synth.make_batch([100, 7, 900, 64], "fp8", "fp8", seed=333, name="mtp-no-host", q_lens=[2, 2, 1, 2])
+    _check_batch(w, use_host_indptr=False, rows_per_split=128, what="q_len <= 2, plan without host indptr")
+    _check_batch(w, use_host_indptr=True, rows_per_split=2048, what="q_len <= 2, one split per sequence")
+
+
+def test_multi_token_rows_equal_single_token_runs():
+    # query rows of a sequence do not interact: each row of a two-row run matches
+    # a one-row run of the same query on the same KV (within the parity bar)
+    lengths = [3000, 17]
+    w2 = synth.make_batch(lengths, "bf16", "fp8", seed=444, name="mtp-pair", q_lens=[2, 2])
+    b2 = dev.upload(w2)
+    out2 = dev.run(dev.plan_for(b2, rows_per_split=512), b2)
+    for r in range(2):
+        w1 = synth.make_batch(lengths, "bf16", "fp8", seed=444, name="mtp-single", q_lens=[1, 1])
+        w1.q = np.ascontiguousarray(w2.q[[r, 2 + r]])
+        b1 = dev.upload(w1)
+        out1 = dev.run(dev.plan_for(b1, rows_per_split=512), b1)
+        torch.cuda.synchronize()
+        a = _bf16_out_to_f64(out2)[[r, 2 + r]]
+        c = _bf16_out_to_f64(out1)
+        _compare(a, c, f"row {r} of q_len 2 vs a one-row run")
+
+
 def test_runs_are_deterministic():
     w = synth.make_batch([3000, 17, 4000], "bf16", "fp8", seed=707, name="det")
     b = dev.upload(w)
@@ -258,6 +315,15 @@ SAMPLE = {
     "bs64_kv8192_fp8": [0, 1, 17, 31, 32, 50, 63],
     "bs256_kv8192_a8w8": [0, 1, 64, 127, 128, 200, 255],
 }
+
+
+@pytest.mark.parametrize("q_len", [2, 4])
+def test_multi_token_full_size_sampled(q_len):
+    # bs 64, KV 8192 fp8 with q_len query rows per sequence, in the launch
+    # configuration the planner picks; sampled sequences against the oracle
+    w = synth.make_batch([8192] * 64, "bf16", "fp8", seed=30 + q_len, name=f"bs64_kv8192_fp8_q{q_len}",
+                         q_lens=[q_len] * 64)
+    _check_batch(w, seq_ids=[0, 1, 31, 63], poison=False, what=f"bs64 kv8192 fp8 q_len {q_len} (sampled)")
 
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
