@@ -57,6 +57,8 @@ def _args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query rows per sequence (multi-token prediction / speculative decoding)")
     ap.add_argument("--rows-per-split", type=int, default=0)
     ap.add_argument("--wgs-per-cu", type=int, default=0)
     ap.add_argument("--hot", action="store_true", help="no KV rotation (cache-resident numbers, secondary)")
@@ -123,15 +125,16 @@ def _measured_traffic(name: str):
 class Timed:
     """One workload resident on the GPU, its plan and rotated KV copies."""
 
-    def __init__(self, name, args, threads):
+    def __init__(self, name, args, threads, q_len=1):
         import torch
         import synth
         from mla_decode_split_amd import device as dev
 
-        self.name = name
+        self.name = name if q_len == 1 else f"{name}_q{q_len}"
+        self.q_len = q_len
         self.spec = synth.WORKLOADS[name]
         t = time.perf_counter()
-        self.w = synth.make_workload(name, threads=threads)
+        self.w = synth.make_workload(name, threads=threads, q_len=q_len)
         self.t_gen = time.perf_counter() - t
         self.kv_bytes = self.w.kv_bytes()
         self.rows = int(self.w.kv_indptr[-1] - self.w.kv_indptr[0])
@@ -207,7 +210,7 @@ class Timed:
 
         d = mla.mla_decode_plan_describe(self.plan)
         return {"workload": self.name, "batch_size": self.spec["bs"], "kv_len": self.spec["kv_len"],
-                "q_dtype": self.w.q_dtype, "kv_dtype": self.w.kv_dtype, "kv_rows": self.rows,
+                "q_len": self.q_len, "q_dtype": self.w.q_dtype, "kv_dtype": self.w.kv_dtype, "kv_rows": self.rows,
                 "kv_bytes": self.kv_bytes, "kv_copies_rotated": self.ncopy, "num_splits": d["num_splits"],
                 "rows_per_split": d["rows_per_split"], "stage2": bool(d["stage2"])}
 
@@ -230,7 +233,7 @@ def main() -> int:
     threads = _host_threads()
     name = args.workload
 
-    h = Timed(name, args, threads)
+    h = Timed(name, args, threads, args.q_len)
     ceiling = h.read_ceiling()
     # throughput: K whole calls back to back, nothing recorded between them
     elapsed = h.time(args.steps, args.warmup)
@@ -261,7 +264,7 @@ def main() -> int:
         "config": cfg,
         "roofline": {"bound": "hbm", "kernel": "mla_split_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _measured_traffic(name), "avg_launch_us": round(split_us, 3),
+                     "traffic": _measured_traffic(h.name), "avg_launch_us": round(split_us, 3),
                      "bytes_per_launch": h.kv_bytes},
         "plan_us": round(1e6 * h.t_plan, 1),
         "input_generation_s": round(h.t_gen, 2),
@@ -279,13 +282,14 @@ def main() -> int:
         import synth
 
         table = []
-        for other in synth.WORKLOADS:
-            t = Timed(other, args, threads)
+        # the five workloads, and the headline shape with several query rows per sequence
+        for other, q_len in [(n, 1) for n in synth.WORKLOADS] + [(DEFAULT_WORKLOAD, 2), (DEFAULT_WORKLOAD, 4)]:
+            t = Timed(other, args, threads, q_len)
             t.read_ceiling(0.05)
             el = t.time(args.steps, args.warmup)
             us = 1e6 * el / args.steps
             d = t.describe()
-            table.append({"workload": other, "us_per_call": round(us, 2),
+            table.append({"workload": t.name, "q_len": q_len, "us_per_call": round(us, 2),
                           "GBs": round(t.kv_bytes / (us * 1e-6) / 1e9, 1),
                           "frac_of_peak": round(t.kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                           "kv_bytes": t.kv_bytes, "num_splits": d["num_splits"],

@@ -33,7 +33,7 @@ _lib = None
 class _Problem(ctypes.Structure):
     _fields_ = [("batch_size", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("qk_dim", ctypes.c_int32),
                 ("v_dim", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("sm_scale", ctypes.c_double)]
+                ("sm_scale", ctypes.c_double), ("logit_cap", ctypes.c_double)]
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -110,7 +110,8 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 def mla_decode(q, kv, qo_indptr, kv_indptr, *, q_dtype="bf16", kv_dtype="bf16", q_scale=None, kv_scale=None,
-               sm_scale=1.0 / 24.0, num_heads=16, qk_dim=576, v_dim=512, seq_ids=None, threads=1, lib=None):
+               sm_scale=1.0 / 24.0, num_heads=16, qk_dim=576, v_dim=512, seq_ids=None, threads=1, lib=None,
+               logit_cap=0.0):
     """fp64 reference output and LSE.
 
     q: uint16 bf16 bits or uint8 fp8 codes, shape [total_q, num_heads, qk_dim].
@@ -125,7 +126,8 @@ def mla_decode(q, kv, qo_indptr, kv_indptr, *, q_dtype="bf16", kv_dtype="bf16", 
     qo = np.ascontiguousarray(qo_indptr, dtype=np.int32)
     kvp = np.ascontiguousarray(kv_indptr, dtype=np.int32)
     total_q = q.shape[0]
-    prob = _Problem(kvp.shape[0] - 1, num_heads, qk_dim, v_dim, DTYPES[q_dtype], DTYPES[kv_dtype], float(sm_scale))
+    prob = _Problem(kvp.shape[0] - 1, num_heads, qk_dim, v_dim, DTYPES[q_dtype], DTYPES[kv_dtype], float(sm_scale),
+                    float(logit_cap))
     qs = None if q_scale is None else np.array([q_scale], dtype=np.float32)
     if kv_dtype == "fp8":
         ks = np.array([kv_scale], dtype=np.float32)
@@ -148,4 +150,4 @@ def decode_workload(w, seq_ids=None, threads=1, lib=None):
     """Oracle on a ``synth.Workload``."""
     return mla_decode(w.q, w.kv, w.qo_indptr, w.kv_indptr, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
                       q_scale=w.q_scale, kv_scale=w.kv_scale, sm_scale=w.sm_scale, seq_ids=seq_ids,
-                      threads=threads, lib=lib)
+                      threads=threads, lib=lib, logit_cap=getattr(w, "logit_cap", 0.0))

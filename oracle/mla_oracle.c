@@ -13,6 +13,11 @@
  *     s_j       = sm_scale * sum_{d < qk_dim} Q[t,h,d] * KV[j,d]
  *     O[t,h,v]  = sum_j softmax_j(s) * KV[j,v]            (v < v_dim)
  *
+ * with, when logit_cap > 0, every scaled score first soft-capped as
+ * s_j <- logit_cap * tanh(s_j / logit_cap).  The pages name logit_cap only as an
+ * argument of a library decode call (submission 753817's fallback, set to 0.0);
+ * the formula is the usual soft-cap reading of that argument.
+ *
  * over the KV rows j in [kv_indptr[b], kv_indptr[b+1]).  Keys are the full
  * qk_dim-wide row, values its first v_dim columns; all heads share the one KV
  * row.  No mask: every query row sees every KV row of its sequence.
@@ -106,6 +111,7 @@ typedef struct {
   int32_t q_dtype;  /* ORACLE_BF16 or ORACLE_FP8_E4M3FN */
   int32_t kv_dtype; /* ORACLE_BF16, ORACLE_FP8_E4M3FN or ORACLE_MXFP4 */
   double sm_scale;
+  double logit_cap; /* > 0: soft-cap of the scaled scores; 0: none */
 } oracle_problem;
 
 /* Decode KV row j (all qk_dim columns) into dst. */
@@ -151,6 +157,7 @@ static void attend_one(const oracle_problem* p, const double* qrow, const double
     double dot = 0.0;
     for (int d = 0; d < D; ++d) dot += qrow[d] * kvrows[j * D + d];
     scores[j] = p->sm_scale * dot;
+    if (p->logit_cap > 0.0) scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);
     if (scores[j] > m) m = scores[j];
   }
   double l = 0.0;
@@ -227,6 +234,7 @@ int oracle_mla_decode(const oracle_problem* p, const void* q, const float* q_sca
                       const int32_t* seq_ids, int n_seq, double* out, double* lse, int nthreads) {
   if (!p || !q || !kv || !qo_indptr || !kv_indptr || !out || !lse) return -1;
   if (p->num_heads <= 0 || p->qk_dim <= 0 || p->v_dim <= 0 || p->v_dim > p->qk_dim) return -1;
+  if (!(p->logit_cap >= 0.0)) return -1;
   if (p->kv_dtype == ORACLE_MXFP4 && p->qk_dim % 32) return -1;
   if (p->kv_dtype != ORACLE_BF16 && !kv_scale) return -1;
   if (p->q_dtype != ORACLE_BF16 && !q_scale) return -1;

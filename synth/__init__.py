@@ -177,6 +177,7 @@ class Workload:
     kv_indptr: np.ndarray
     sm_scale: float = SM_SCALE
     meta: dict = field(default_factory=dict)
+    logit_cap: float = 0.0             # > 0: scores soft-capped as cap * tanh(s / cap)
 
     @property
     def batch_size(self) -> int:
@@ -263,7 +264,10 @@ def workload_lengths(name: str) -> np.ndarray:
     return np.full(spec["bs"], spec["kv_len"], dtype=np.int32)
 
 
-def make_workload(name: str, threads: int | None = None) -> Workload:
+def make_workload(name: str, threads: int | None = None, q_len: int = 1) -> Workload:
+    """One of the named workloads; with q_len > 1 every sequence gets q_len
+    query rows over the same KV (named ``<name>_q<q_len>``)."""
     spec = WORKLOADS[name]
-    return make_batch(workload_lengths(name), spec["q_dtype"], spec["kv_dtype"], spec["seed"], name=name,
-                      threads=threads)
+    q_lens = None if q_len == 1 else [q_len] * spec["bs"]
+    return make_batch(workload_lengths(name), spec["q_dtype"], spec["kv_dtype"], spec["seed"],
+                      name=name if q_len == 1 else f"{name}_q{q_len}", threads=threads, q_lens=q_lens)

@@ -200,6 +200,50 @@ def test_two_rows_closed_form(rng):
         assert lse[0, h] == pytest.approx(max(s1, s2) + math.log1p(math.exp(-abs(s1 - s2))), rel=1e-13)
 
 
+# ----------------------------------------------------------------- logit soft-cap
+
+def test_soft_capped_two_rows_closed_form(rng):
+    # with a cap, the two weights are sigmoids of the difference of the capped scores
+    cap = 0.75
+    q, kv, qo, kvp = _rand_batch(rng, [2])
+    out, lse = oracle.mla_decode(q, kv, qo, kvp, logit_cap=cap)
+    k = _f(kv)
+    for h in range(H):
+        qq = _f(q[0, h])
+        s1 = float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qq, k[0])) / 24)
+        s2 = float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qq, k[1])) / 24)
+        c1, c2 = cap * math.tanh(s1 / cap), cap * math.tanh(s2 / cap)
+        w1 = 1.0 / (1.0 + math.exp(c2 - c1))
+        assert np.allclose(out[0, h], w1 * k[0, :V] + (1.0 - w1) * k[1, :V], rtol=1e-12, atol=1e-13)
+        assert lse[0, h] == pytest.approx(max(c1, c2) + math.log1p(math.exp(-abs(c1 - c2))), rel=1e-12)
+
+
+def test_soft_cap_far_above_the_scores_changes_nothing(rng):
+    # cap * tanh(s / cap) = s - s^3 / (3 cap^2) + ...: with |s| < 10 and cap 1e5
+    # the scores move by < 4e-8 relative
+    q, kv, qo, kvp = _rand_batch(rng, [5, 40])
+    plain, lse0 = oracle.mla_decode(q, kv, qo, kvp)
+    capped, lse1 = oracle.mla_decode(q, kv, qo, kvp, logit_cap=1e5)
+    assert np.allclose(capped, plain, rtol=1e-7, atol=1e-9)
+    assert np.allclose(lse1, lse0, rtol=1e-7)
+
+
+def test_soft_cap_saturation_gives_mean_of_values(rng):
+    # every score far above the cap: tanh saturates, the capped scores are all
+    # equal (to cap up to ~1e-40), so the output is the mean of the V rows
+    n = 11
+    qf = np.zeros((1, H, D))
+    qf[0, :, 512] = 64.0
+    kvf = rng.standard_normal((n, D))
+    kvf[:, 512] = 64.0 + rng.integers(0, 64, size=n)  # scores 64*[64, 128)/24 > 170
+    q, kv = _bf16(qf), _bf16(kvf)
+    out, lse = oracle.mla_decode(q, kv, [0, 1], [0, n], logit_cap=2.0)
+    mean = _f(kv)[:, :V].mean(axis=0)
+    for h in range(H):
+        assert np.allclose(out[0, h], mean, rtol=1e-13, atol=1e-15)
+    assert np.allclose(lse[0], 2.0 + math.log(n), rtol=1e-13)
+
+
 def test_empty_sequence_gives_zero_and_minus_inf(rng):
     q, kv, qo, kvp = _rand_batch(rng, [3, 0, 2])
     out, lse = oracle.mla_decode(q, kv, qo, kvp)

@@ -38,6 +38,10 @@ MUTANTS = {
     "q_head_stride": ("const int64_t base = (t * p->num_heads + h) * (int64_t)D;",
                       "const int64_t base = (t * p->num_heads) * (int64_t)D + h;"),
     "normalisation_dropped": ("for (int v = 0; v < V; ++v) out[v] /= l;", ""),
+    "soft_cap_outer_factor_dropped": ("scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);",
+                                      "scores[j] = tanh(scores[j] / p->logit_cap);"),
+    "soft_cap_before_sm_scale": ("scores[j] = p->sm_scale * dot;\n    if (p->logit_cap > 0.0) scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);",
+                                 "scores[j] = dot;\n    if (p->logit_cap > 0.0) scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);\n    scores[j] *= p->sm_scale;"),
 }
 
 
@@ -121,6 +125,18 @@ def pin_battery(lib):
     ob, _ = oracle.mla_decode(qq, _bf16(indep), [0, 1], [0, 20], lib=lib)
     if not (np.array_equal(dec, indep) and np.array_equal(o4, ob)):
         failed.append("mxfp4_folding")
+
+    # soft-cap: two KV rows in closed form (sigmoid of the capped score difference)
+    cap = 0.6
+    q2 = _bf16(rng.standard_normal((1, H, D)))
+    k2 = _bf16(rng.standard_normal((2, D)))
+    o, _ = oracle.mla_decode(q2, k2, [0, 1], [0, 2], lib=lib, logit_cap=cap)
+    sc2 = SM * (_f(q2)[0] @ _f(k2).T)  # [H, 2]
+    c = cap * np.tanh(sc2 / cap)
+    w1 = 1.0 / (1.0 + np.exp(c[:, 1] - c[:, 0]))
+    want = w1[:, None] * _f(k2)[0, :V] + (1.0 - w1)[:, None] * _f(k2)[1, :V]
+    if not np.allclose(o[0], want, rtol=1e-11, atol=1e-13):
+        failed.append("soft_cap_two_rows")
 
     # split recombination of LSE-weighted pieces
     qr = np.repeat(qb[1:2], 3, axis=0)
