@@ -68,6 +68,10 @@ typedef struct mla_problem {
                          qo_indptr[b+1] - qo_indptr[b] in [0, max_q_len], every row attending
                          to all KV rows of its sequence with no mask - multi-token prediction
                          or speculative decoding).  Larger values: MLA_ERR_UNSUPPORTED */
+  float logit_cap;    /* 0: none; > 0 (finite): every scaled score s is soft-capped to
+                         logit_cap * tanh(s / logit_cap) before the softmax - the logit_cap
+                         argument of the library decode call on submission 753817's page,
+                         read as the usual soft-cap (the page passes 0.0) */
 } mla_problem;
 
 /* Optional planner overrides (NULL = planner's choice for every field). */

@@ -26,7 +26,8 @@ class mla_problem(ctypes.Structure):
     _fields_ = [("batch_size", ctypes.c_int32), ("total_q", ctypes.c_int32), ("total_kv", ctypes.c_int64),
                 ("num_heads", ctypes.c_int32), ("qk_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("num_cus", ctypes.c_int32), ("max_q_len", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+                ("logit_cap", ctypes.c_float)]
 
 
 class mla_plan_options(ctypes.Structure):
@@ -119,9 +120,10 @@ def mla_status_string(status: int) -> str:
 
 
 def make_problem(batch_size, total_kv, q_dtype="bf16", kv_dtype="bf16", total_q=None, num_heads=16, qk_dim=576,
-                 v_dim=512, sm_scale=1.0 / 24.0, num_cus=0, max_q_len=0) -> mla_problem:
+                 v_dim=512, sm_scale=1.0 / 24.0, num_cus=0, max_q_len=0, logit_cap=0.0) -> mla_problem:
     return mla_problem(batch_size, batch_size if total_q is None else total_q, total_kv, num_heads, qk_dim, v_dim,
-                       DTYPES.get(q_dtype, q_dtype), DTYPES.get(kv_dtype, kv_dtype), sm_scale, num_cus, max_q_len)
+                       DTYPES.get(q_dtype, q_dtype), DTYPES.get(kv_dtype, kv_dtype), sm_scale, num_cus, max_q_len,
+                       logit_cap)
 
 
 class Plan:

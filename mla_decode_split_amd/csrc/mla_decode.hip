@@ -519,6 +519,7 @@ struct SplitParams {
   int32_t batch;
   int32_t rows_per_wg;
   float sm_scale;
+  float logit_cap;  // > 0: scaled scores soft-capped as cap * tanh(s / cap)
 };
 
 // Query operand of S^T = K Q^T for the dims this wave multiplies.  The four
@@ -875,15 +876,31 @@ __device__ inline uint8_t* max_ptr(uint8_t* st, uint8_t* pb, int t, int h) {
 //   value columns.
 // Below the slack bf16 P and the fp32 sums hold p = 2^(t - m_run) without loss,
 // and the final normalisation by the running sum is unchanged.
+// Logit soft-cap in the units the scores are summed in: a raw score v (sum of
+// products, before the base-2 factor c) becomes U tanh(v / U) with U = cap *
+// log2(e) / c, so that c times it is cap * tanh(s / cap) in base 2 for the
+// natural score s = c v / log2(e).  tanh(y) = 1 - 2 / (e^(2y) + 1), with e^(2y)
+// = 2^(v * k), k = 2 c / cap; it saturates to +-1 where the exponential
+// overflows or underflows.
+template <int QL, bool ON>
+struct SoftCap {
+  static constexpr bool on = ON;
+  float u[QL], k[QL];
+  __device__ inline float apply(float v, int t) const {
+    const float e = __builtin_amdgcn_exp2f(v * k[t]);
+    return u[t] * fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+  }
+};
+
 struct TileScores {
   float sv[2];  // raw scores of KV rows 4g + w and 16 + 4g + w, head m (-inf when masked)
   float p[2];   // their probabilities against m_run as it was when they were posted
 };
 
-template <int QF, int KF, int QL, bool MASK>
+template <int QF, int KF, int QL, bool CAP, bool MASK>
 __device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const QOperand<QF, KF> (&qo)[QL],
                                   const LaneOffs<KF>& lo, const WaveState (&ws)[QL], int w, int m, int g, int sdelta,
-                                  int valid, const float (&c)[QL], TileScores (&ts)[QL]) {
+                                  int valid, const float (&c)[QL], const SoftCap<QL, CAP>& cap, TileScores (&ts)[QL]) {
   const int lane = threadIdx.x & 63;
   {
     f32x4 part[QL][2];
@@ -907,6 +924,7 @@ __device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const Q
       v += xt[((2 + blk) * 4 + w) * 64 + lane];
       v += xt[((4 + blk) * 4 + w) * 64 + lane];
       v += xt[((6 + blk) * 4 + w) * 64 + lane];
+      if constexpr (CAP) v = cap.apply(v, t);
       ts[t].sv[blk] = (MASK && 16 * blk + 4 * g + w >= valid) ? -INFINITY : v;
     }
     // the base-2 score is sv * c with c > 0
@@ -985,7 +1003,7 @@ __device__ inline void set_priority(int prio) {
 // One piece: rows [r0, r0 + n) of a sequence whose query rows are qrow0 ..
 // qrow0 + nq - 1 (nq in [1, QL]; the operands of tokens past nq repeat the
 // last row and their results are dropped).
-template <int QF, int KF, int QL>
+template <int QF, int KF, int QL, bool CAP>
 __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf,
                             const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow0, int nq, int64_t r0,
                             int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
@@ -1099,6 +1117,14 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   float cs[QL];
 #pragma unroll
   for (int t = 0; t < QL; ++t) cs[t] = score_scale * qop[t].scale;
+  SoftCap<QL, CAP> cap;
+#pragma unroll
+  for (int t = 0; t < QL; ++t) {
+    // c = 0 (a zero q or KV scale): every score is 0 and stays 0
+    const bool live = CAP && cs[t] > 0.f;
+    cap.u[t] = live ? p.logit_cap * kLog2e / cs[t] : 0.f;
+    cap.k[t] = live ? 2.f * cs[t] / p.logit_cap : 0.f;
+  }
   const int last_valid = n - (ntiles - 1) * kTile;
   auto stage = [&](int i) { return ring + (i % NS) * G::kStageBytes; };
   // probability records of tokens >= 1: one set per tile parity
@@ -1108,23 +1134,24 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   priority(0);
   advance(0);
   if (nfull > 0)
-    score_tile<QF, KF, QL, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), kTile, cs, ts);
+    score_tile<QF, KF, QL, CAP, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), kTile, cs, cap, ts);
   else
-    score_tile<QF, KF, QL, true>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), last_valid, cs, ts);
+    score_tile<QF, KF, QL, CAP, true>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), last_valid, cs, cap,
+                                 ts);
   refill(0);
   for (int i = 1; i < nfull; ++i) {
     priority(i);
     advance(i);
     finish_tile<QF, KF, QL, false>(stage(i - 1), pbuf_of(i - 1), lo, ws, w, m, g, sdelta_of(i - 1), kTile, cs, ts);
-    score_tile<QF, KF, QL, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile, cs, ts);
+    score_tile<QF, KF, QL, CAP, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile, cs, cap, ts);
     refill(i);
   }
   if (nfull > 0 && nfull < ntiles) {  // the partial last tile
     advance(nfull);
     finish_tile<QF, KF, QL, false>(stage(nfull - 1), pbuf_of(nfull - 1), lo, ws, w, m, g, sdelta_of(nfull - 1), kTile,
                                    cs, ts);
-    score_tile<QF, KF, QL, true>(stage(nfull), pbuf_of(nfull), xchg, qop, lo, ws, w, m, g, sdelta_of(nfull),
-                                 last_valid, cs, ts);
+    score_tile<QF, KF, QL, CAP, true>(stage(nfull), pbuf_of(nfull), xchg, qop, lo, ws, w, m, g, sdelta_of(nfull),
+                                 last_valid, cs, cap, ts);
   }
   lds_barrier();  // the last tile's probabilities are in LDS
   if (nfull < ntiles)
@@ -1168,7 +1195,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   }
 }
 
-template <int QF, int KF, int QL>
+template <int QF, int KF, int QL, bool CAP>
 __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(
     Ring<KF, QL>::kWgsPerCu, Ring<KF, QL>::kWgsPerCu))) void mla_split_kernel(SplitParams p) {
   using G = Geom<KF>;
@@ -1231,7 +1258,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
-    split_piece<QF, KF, QL>(p, ring, xchg, pbuf, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
+    split_piece<QF, KF, QL, CAP>(p, ring, xchg, pbuf, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
                             r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
     lds_barrier();  // the next piece refills the ring
   }
@@ -1455,15 +1482,23 @@ int min_rows_for(int kv_dtype) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-template <int QF, int KF>
-hipError_t launch_split(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
+template <int QF, int KF, bool CAP>
+void launch_split_cap(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
   const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads);
   if (pl->ql == 1)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP>), grid, block, 0, st, sp);
   else if (pl->ql == 2)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2, CAP>), grid, block, 0, st, sp);
   else
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4, CAP>), grid, block, 0, st, sp);
+}
+
+template <int QF, int KF>
+hipError_t launch_split(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
+  if (pl->prob.logit_cap > 0.f)
+    launch_split_cap<QF, KF, true>(pl, sp, st);
+  else
+    launch_split_cap<QF, KF, false>(pl, sp, st);
   return hipGetLastError();
 }
 
@@ -1495,6 +1530,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   if (pr->num_heads != kHeads || pr->qk_dim != kQK || pr->v_dim != kV) return MLA_ERR_UNSUPPORTED;
   // query rows per sequence: one, or up to max_q_len (2 or 4 kernels; 3 runs on the 4-token one)
   if (pr->max_q_len < 0 || pr->max_q_len > 4) return MLA_ERR_UNSUPPORTED;
+  if (!(pr->logit_cap >= 0.f) || !(pr->logit_cap < INFINITY)) return MLA_ERR_INVALID_ARG;
   const int ql = pr->max_q_len <= 1 ? 1 : pr->max_q_len == 2 ? 2 : 4;
   if (ql == 1 && pr->total_q != pr->batch_size) return MLA_ERR_UNSUPPORTED;  // one query token per sequence
   if (ql > 1 && (pr->total_q < 1 || (int64_t)pr->total_q > (int64_t)pr->batch_size * pr->max_q_len))
@@ -1667,6 +1703,7 @@ mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, cons
   sp->batch = pr.batch_size;
   sp->rows_per_wg = pl->rows_per_wg;
   sp->sm_scale = pr.sm_scale;
+  sp->logit_cap = pr.logit_cap;
   mp->part_o = sp->part_o;
   mp->part_lse = sp->part_lse;
   mp->qo_indptr = qo_indptr;

@@ -25,6 +25,7 @@ class DeviceBatch:
     kv_indptr: torch.Tensor
     kv_indptr_host: np.ndarray
     max_q_len: int
+    logit_cap: float
     q_dtype: str
     kv_dtype: str
     sm_scale: float
@@ -65,13 +66,15 @@ def upload(w, device="cuda") -> DeviceBatch:
                        kv_indptr=_to_dev(w.kv_indptr.astype(np.int32), device),
                        kv_indptr_host=np.ascontiguousarray(w.kv_indptr, dtype=np.int32),
                        max_q_len=int(np.diff(np.asarray(w.qo_indptr, dtype=np.int64)).max(initial=0)),
+                       logit_cap=float(getattr(w, "logit_cap", 0.0)),
                        q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, sm_scale=float(w.sm_scale))
 
 
 def plan_for(batch: DeviceBatch, rows_per_split: int = 0, wgs_per_cu: int = 0, use_host_indptr: bool = True,
              num_cus: int = 0) -> Plan:
     prob = make_problem(batch.batch_size, batch.total_kv, batch.q_dtype, batch.kv_dtype, total_q=batch.total_q,
-                        sm_scale=batch.sm_scale, num_cus=num_cus, max_q_len=batch.max_q_len)
+                        sm_scale=batch.sm_scale, num_cus=num_cus, max_q_len=batch.max_q_len,
+                        logit_cap=batch.logit_cap)
     opts = mla_plan_options(rows_per_split, wgs_per_cu) if (rows_per_split or wgs_per_cu) else None
     return mla_decode_plan(prob, opts, batch.kv_indptr_host if use_host_indptr else None)
 

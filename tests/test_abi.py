@@ -179,6 +179,15 @@ def test_several_query_rows_argument_errors():
     assert _status(mla.mla_decode_plan, prob) == mla.MLA_OK
 
 
+def test_logit_cap_argument_errors():
+    for bad in (-1.0, float("nan"), float("inf")):
+        prob = mla.make_problem(4, 100, num_cus=256, logit_cap=bad)
+        assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG, bad
+    for ok in (0.0, 1e-3, 30.0):
+        prob = mla.make_problem(4, 100, num_cus=256, logit_cap=ok)
+        assert _status(mla.mla_decode_plan, prob) == mla.MLA_OK, ok
+
+
 def test_plan_argument_errors():
     unsupported = [
         dict(num_heads=8), dict(qk_dim=512), dict(v_dim=576), dict(total_q=8),

@@ -232,6 +232,32 @@ def test_multi_token_rows_equal_single_token_runs():
         _compare(a, c, f"row {r} of q_len 2 vs a one-row run")
 
 
+# ------------------------------------------------------------- logit soft-cap
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", COMBOS)
+def test_soft_cap_all_formats(q_dtype, kv_dtype):
+    # scores here are about N(0, 1): a cap of 1 bends most of them
+    w = synth.make_batch(EDGE_LENGTHS, q_dtype, kv_dtype, seed=121, name="softcap")
+    w.logit_cap = 1.0
+    _check_batch(w, what=f"logit_cap 1.0 {q_dtype}/{kv_dtype}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+def test_soft_cap_with_query_rows_and_splits(kv_dtype):
+    w = synth.make_batch([700, 0, 33, 1000, 257], "bf16", kv_dtype, seed=131, name="softcap-mtp", q_lens=[2, 1, 2, 0, 2])
+    w.logit_cap = 0.5
+    _check_batch(w, rows_per_split=96, what=f"logit_cap 0.5, q_len <= 2, rows_per_split=96 kv={kv_dtype}")
+
+
+def test_soft_cap_saturating_scores():
+    # queries scaled by 16 (exact in bf16): scores about N(0, 256), most of them
+    # far past the cap of 4, where tanh saturates
+    w = synth.make_batch([1000, 64, 4000], "bf16", "fp8", seed=141, name="softcap-sat")
+    w.q = synth.bf16_bits(synth.bf16_to_f32(w.q) * 16.0)
+    w.logit_cap = 4.0
+    _check_batch(w, rows_per_split=256, what="logit_cap 4, saturating scores")
+
+
 def test_runs_are_deterministic():
     w = synth.make_batch([3000, 17, 4000], "bf16", "fp8", seed=707, name="det")
     b = dev.upload(w)
