@@ -61,6 +61,8 @@ def _bind(lib):
     lib.oracle_decode_mxfp4.argtypes = [vp, vp, i64, i32, vp]
     lib.oracle_mla_decode.argtypes = [ctypes.POINTER(_Problem), vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32]
     lib.oracle_mla_decode.restype = i32
+    lib.oracle_mla_decode_paged.argtypes = [ctypes.POINTER(_Problem), vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32]
+    lib.oracle_mla_decode_paged.restype = i32
     return lib
 
 
@@ -111,13 +113,15 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 def mla_decode(q, kv, qo_indptr, kv_indptr, *, q_dtype="bf16", kv_dtype="bf16", q_scale=None, kv_scale=None,
                sm_scale=1.0 / 24.0, num_heads=16, qk_dim=576, v_dim=512, seq_ids=None, threads=1, lib=None,
-               logit_cap=0.0):
+               logit_cap=0.0, kv_indices=None):
     """fp64 reference output and LSE.
 
     q: uint16 bf16 bits or uint8 fp8 codes, shape [total_q, num_heads, qk_dim].
     kv: uint16 [total_kv, qk_dim] (bf16), uint8 [total_kv, qk_dim] (fp8) or
         uint8 [total_kv, qk_dim/2] (mxfp4 packed).
     kv_scale: fp32 scalar for fp8, uint8 [total_kv, qk_dim/32] for mxfp4.
+    kv_indices: None, or int32 [kv_indptr[-1]]: KV row j of the CSR space is
+        kv[kv_indices[j]] (paged KV, page size 1).
     Returns (out [total_q, num_heads, v_dim] float64, lse [total_q, num_heads]);
     rows of sequences not in ``seq_ids`` are NaN."""
     lib = lib or load()
@@ -139,8 +143,15 @@ def mla_decode(q, kv, qo_indptr, kv_indptr, *, q_dtype="bf16", kv_dtype="bf16", 
     out = np.full((total_q, num_heads, v_dim), np.nan, dtype=np.float64)
     lse = np.full((total_q, num_heads), np.nan, dtype=np.float64)
     n_seq = prob.batch_size if ids is None else ids.shape[0]
-    rc = lib.oracle_mla_decode(ctypes.byref(prob), _p(q), _p(qs), _p(kv), _p(ks), _p(qo), _p(kvp), _p(ids), n_seq,
-                               _p(out), _p(lse), int(threads))
+    if kv_indices is None:
+        rc = lib.oracle_mla_decode(ctypes.byref(prob), _p(q), _p(qs), _p(kv), _p(ks), _p(qo), _p(kvp), _p(ids),
+                                   n_seq, _p(out), _p(lse), int(threads))
+    else:
+        ki = np.ascontiguousarray(kv_indices, dtype=np.int32)
+        if ki.shape[0] < int(kvp[-1]) or (ki.size and (ki.min() < 0 or ki.max() >= kv.shape[0])):
+            raise ValueError("kv_indices must cover the CSR rows and index rows of kv")
+        rc = lib.oracle_mla_decode_paged(ctypes.byref(prob), _p(q), _p(qs), _p(kv), _p(ks), _p(qo), _p(kvp), _p(ki),
+                                         _p(ids), n_seq, _p(out), _p(lse), int(threads))
     if rc != 0:
         raise RuntimeError(f"oracle_mla_decode failed ({rc})")
     return out, lse
@@ -150,4 +161,5 @@ def decode_workload(w, seq_ids=None, threads=1, lib=None):
     """Oracle on a ``synth.Workload``."""
     return mla_decode(w.q, w.kv, w.qo_indptr, w.kv_indptr, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
                       q_scale=w.q_scale, kv_scale=w.kv_scale, sm_scale=w.sm_scale, seq_ids=seq_ids,
-                      threads=threads, lib=lib, logit_cap=getattr(w, "logit_cap", 0.0))
+                      threads=threads, lib=lib, logit_cap=getattr(w, "logit_cap", 0.0),
+                      kv_indices=getattr(w, "kv_indices", None))

@@ -27,6 +27,11 @@
  * Quantised inputs are used through their decoded values for both K and V:
  *   fp8 E4M3FN   value(code) * scale            (one fp32 scale per tensor)
  *   MXFP4        value_E2M1(nibble) * 2^(E8M0 - 127)   (one scale per 32 columns)
+ * Paged KV (page size 1, the layout of the library decode call on submission
+ * 753817's page, which passes kv_indices with page_size 1): the rows of
+ * sequence b are KV[kv_indices[j]] for j in [kv_indptr[b], kv_indptr[b+1]).
+ * Without kv_indices they are KV[j].
+ *
  * The fp8 a8w8 reference on the template page multiplies the two per-tensor
  * scales into the fp8 product (torch._scaled_mm with scale_a, scale_b), which
  * is the same number as decoding each operand first.
@@ -176,7 +181,7 @@ typedef struct {
   const oracle_problem* p;
   const void *q, *kv, *kv_scale;
   const float* q_scale;
-  const int32_t *qo_indptr, *kv_indptr, *seq_ids;
+  const int32_t *qo_indptr, *kv_indptr, *kv_indices, *seq_ids;
   int n_seq;
   double *out, *lse;
   int next; /* shared work counter, guarded by mu */
@@ -211,7 +216,10 @@ static void* worker(void* arg) {
         break;
       }
     }
-    for (int64_t j = 0; j < n; ++j) decode_kv_row(p, sh->kv, sh->kv_scale, j0 + j, kvrows + j * D);
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t row = sh->kv_indices ? (int64_t)sh->kv_indices[j0 + j] : j0 + j;
+      decode_kv_row(p, sh->kv, sh->kv_scale, row, kvrows + j * D);
+    }
     for (int64_t t = sh->qo_indptr[b]; t < sh->qo_indptr[b + 1]; ++t)
       for (int h = 0; h < H; ++h) {
         decode_q_row(p, sh->q, sh->q_scale, t, h, qrow);
@@ -229,9 +237,24 @@ static void* worker(void* arg) {
  * query row: out[(t*num_heads + h)*v_dim + v], lse[t*num_heads + h]; entries of
  * sequences not listed are left untouched.  Returns 0, or a negative value on
  * bad arguments / allocation failure. */
+int oracle_mla_decode_paged(const oracle_problem* p, const void* q, const float* q_scale, const void* kv,
+                            const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* seq_ids, int n_seq, double* out, double* lse,
+                            int nthreads);
+
 int oracle_mla_decode(const oracle_problem* p, const void* q, const float* q_scale, const void* kv,
                       const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr,
                       const int32_t* seq_ids, int n_seq, double* out, double* lse, int nthreads) {
+  return oracle_mla_decode_paged(p, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, NULL, seq_ids, n_seq, out, lse,
+                                 nthreads);
+}
+
+/* The same with KV row j of the CSR space read from KV[kv_indices[j]] (NULL:
+ * KV[j]); the caller guarantees every index is a row of kv. */
+int oracle_mla_decode_paged(const oracle_problem* p, const void* q, const float* q_scale, const void* kv,
+                            const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* seq_ids, int n_seq, double* out, double* lse,
+                            int nthreads) {
   if (!p || !q || !kv || !qo_indptr || !kv_indptr || !out || !lse) return -1;
   if (p->num_heads <= 0 || p->qk_dim <= 0 || p->v_dim <= 0 || p->v_dim > p->qk_dim) return -1;
   if (!(p->logit_cap >= 0.0)) return -1;
@@ -248,6 +271,7 @@ int oracle_mla_decode(const oracle_problem* p, const void* q, const float* q_sca
   sh.kv_scale = kv_scale;
   sh.qo_indptr = qo_indptr;
   sh.kv_indptr = kv_indptr;
+  sh.kv_indices = kv_indices;
   sh.seq_ids = seq_ids;
   sh.n_seq = n_seq;
   sh.out = out;

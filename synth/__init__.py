@@ -178,6 +178,7 @@ class Workload:
     sm_scale: float = SM_SCALE
     meta: dict = field(default_factory=dict)
     logit_cap: float = 0.0             # > 0: scores soft-capped as cap * tanh(s / cap)
+    kv_indices: np.ndarray | None = None  # paged KV (page size 1): CSR row j is kv[kv_indices[j]]
 
     @property
     def batch_size(self) -> int:
@@ -189,6 +190,12 @@ class Workload:
 
     @property
     def total_kv(self) -> int:
+        """Rows of the CSR space (of the KV buffer when not paged)."""
+        return int(self.kv.shape[0]) if self.kv_indices is None else int(self.kv_indices.shape[0])
+
+    @property
+    def kv_rows(self) -> int:
+        """Rows of the KV buffer."""
         return int(self.kv.shape[0])
 
     def kv_bytes(self) -> int:
@@ -243,6 +250,34 @@ def make_batch(lengths, q_dtype: str, kv_dtype: str, seed: int, name: str = "cus
     return Workload(name=name, q_dtype=q_dtype, kv_dtype=kv_dtype, q=q, q_scale=q_scale, kv=kv,
                     kv_scale=kv_scale, qo_indptr=qo_indptr, kv_indptr=kv_indptr,
                     meta={"seed": seed, "lengths": lengths, "q_lens": np.diff(qo_indptr)})
+
+
+def page_workload(w: Workload, seed: int, spare_rows: int = 0, threads: int | None = None) -> Workload:
+    """The same batch with its KV rows scattered over a larger buffer (paged
+    KV, page size 1): a seeded random injective map sends CSR row j to
+    physical row kv_indices[j] of a buffer of total_kv + spare_rows rows; the
+    rows no index names hold fresh draws of the same format, so a wrong index
+    reads different data.  Only MXFP4 scale rows move with their rows."""
+    n = w.total_kv
+    rows = n + spare_rows
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x9A6E]))
+    kv_indices = rng.permutation(rows)[:n].astype(np.int32)
+    filler = make_batch([rows], "bf16", w.kv_dtype, seed=seed + 1000003, threads=threads)
+    kv = filler.kv.copy()
+    kv[kv_indices] = w.kv
+    kv_scale = w.kv_scale
+    if w.kv_dtype == "mxfp4":
+        kv_scale = filler.kv_scale.copy()
+        kv_scale[kv_indices] = w.kv_scale
+    elif w.kv_dtype == "fp8":
+        # the filler was quantised with its own scale: re-encode nothing, the
+        # per-tensor scale of the batch applies to every row of the buffer
+        kv_scale = w.kv_scale
+    out = Workload(name=w.name + "_paged", q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, q=w.q, q_scale=w.q_scale, kv=kv,
+                   kv_scale=kv_scale, qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr, sm_scale=w.sm_scale,
+                   meta=dict(w.meta, paged_seed=seed, spare_rows=spare_rows), logit_cap=w.logit_cap,
+                   kv_indices=kv_indices)
+    return out
 
 
 # The five decode workloads: (batch size, KV length or "ragged", q dtype, KV dtype, seed).

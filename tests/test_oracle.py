@@ -375,6 +375,30 @@ def test_multiple_query_rows_per_sequence(rng):
     assert np.allclose(out, ref, rtol=1e-11, atol=1e-13)
 
 
+# ----------------------------------------------------------------- paged KV (page size 1)
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+def test_paged_rows_equal_contiguous_rows(kv_dtype):
+    # the same batch with its rows scattered over a larger buffer through a
+    # random injective map gives exactly the contiguous result
+    w = synth.make_batch([5, 0, 40, 17], "bf16", kv_dtype, seed=7, q_lens=[1, 2, 2, 1])
+    pw = synth.page_workload(w, seed=8, spare_rows=30)
+    assert pw.kv_rows == w.total_kv + 30 and not np.array_equal(pw.kv[: w.total_kv], w.kv)
+    a, la = oracle.decode_workload(w)
+    b, lb = oracle.decode_workload(pw)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_paged_identity_and_repeated_rows(rng):
+    q, kv, qo, kvp = _rand_batch(rng, [6, 3])
+    ident = np.arange(9, dtype=np.int32)
+    assert np.array_equal(oracle.mla_decode(q, kv, qo, kvp, kv_indices=ident)[0], oracle.mla_decode(q, kv, qo, kvp)[0])
+    # two CSR rows naming one physical row: the same as that row stored twice
+    idx = np.array([0, 1, 2, 2, 4, 5, 6, 7, 8], dtype=np.int32)
+    dup = kv[idx]
+    assert np.array_equal(oracle.mla_decode(q, kv, qo, kvp, kv_indices=idx)[0], oracle.mla_decode(q, dup, qo, kvp)[0])
+
+
 # ----------------------------------------------------------------- quantised formats
 
 def test_fp8_kv_folding_identity(rng):

@@ -38,6 +38,8 @@ MUTANTS = {
     "q_head_stride": ("const int64_t base = (t * p->num_heads + h) * (int64_t)D;",
                       "const int64_t base = (t * p->num_heads) * (int64_t)D + h;"),
     "normalisation_dropped": ("for (int v = 0; v < V; ++v) out[v] /= l;", ""),
+    "paged_index_ignored": ("const int64_t row = sh->kv_indices ? (int64_t)sh->kv_indices[j0 + j] : j0 + j;",
+                            "const int64_t row = j0 + j;"),
     "soft_cap_outer_factor_dropped": ("scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);",
                                       "scores[j] = tanh(scores[j] / p->logit_cap);"),
     "soft_cap_before_sm_scale": ("scores[j] = p->sm_scale * dot;\n    if (p->logit_cap > 0.0) scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);",
@@ -137,6 +139,15 @@ def pin_battery(lib):
     want = w1[:, None] * _f(k2)[0, :V] + (1.0 - w1)[:, None] * _f(k2)[1, :V]
     if not np.allclose(o[0], want, rtol=1e-11, atol=1e-13):
         failed.append("soft_cap_two_rows")
+
+    # paged KV: rows scattered through a permutation read back in CSR order
+    perm = rng.permutation(int(kvp[-1])).astype(np.int32)
+    scattered = np.empty_like(kb)
+    scattered[perm] = kb
+    o, _ = oracle.mla_decode(qb, scattered, qo, kvp, lib=lib, kv_indices=perm)
+    o2, _ = oracle.mla_decode(qb, kb, qo, kvp, lib=lib)
+    if not np.array_equal(o, o2):
+        failed.append("paged_permutation")
 
     # split recombination of LSE-weighted pieces
     qr = np.repeat(qb[1:2], 3, axis=0)
