@@ -72,6 +72,11 @@ typedef struct mla_problem {
                          logit_cap * tanh(s / logit_cap) before the softmax - the logit_cap
                          argument of the library decode call on submission 753817's page,
                          read as the usual soft-cap (the page passes 0.0) */
+  int32_t kv_paged;   /* 0: sequence b's KV rows are rows [kv_indptr[b], kv_indptr[b+1]) of kv;
+                         1: paged KV with page size 1 (the layout of the library decode call
+                         on submission 753817's page, page_size 1 with kv_indices): CSR row j
+                         is row kv_indices[j] of kv, and runs go through the _paged entry
+                         points.  bf16 and fp8 KV; MXFP4: MLA_ERR_UNSUPPORTED */
 } mla_problem;
 
 /* Optional planner overrides (NULL = planner's choice for every field). */
@@ -151,6 +156,29 @@ mla_status mla_decode_plan(const mla_problem* problem, const mla_plan_options* o
 mla_status mla_decode_run(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
                           const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_run for a plan made with kv_paged = 1.  The arguments are those of
+ * mla_decode_run, with total_kv counting CSR rows, plus:
+ *   kv_rows    rows of the kv buffer ([kv_rows][576] bf16 or fp8 codes); at most
+ *              0xFFFFF000 bytes of rows (larger buffers: MLA_ERR_UNSUPPORTED).
+ *   kv_indices device int32 [total_kv], 4-byte aligned: CSR row j of the plan is
+ *              row kv_indices[j] of kv.  An index outside [0, kv_rows) gives
+ *              undefined output for its sequence, but every read stays inside the
+ *              kv buffer (reads past it return zero).
+ * A contiguous plan, or a NULL kv_indices, is MLA_ERR_INVALID_ARG (and a paged
+ * plan passed to mla_decode_run or mla_decode_split is too).
+ */
+mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
+                                const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
+                                const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Stage 1 alone of mla_decode_run_paged (stage 2 is mla_decode_merge, unchanged). */
+mla_status mla_decode_split_paged(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
+                                  const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
+                                  const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * The two stages of mla_decode_run as separate calls, for callers that put

@@ -27,7 +27,7 @@ class mla_problem(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("qk_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("num_cus", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
-                ("logit_cap", ctypes.c_float)]
+                ("logit_cap", ctypes.c_float), ("kv_paged", ctypes.c_int32)]
 
 
 class mla_plan_options(ctypes.Structure):
@@ -67,6 +67,10 @@ def _lib_handle():
         lib.mla_decode_run.restype = i32
         lib.mla_decode_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_split.restype = i32
+        lib.mla_decode_run_paged.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+        lib.mla_decode_run_paged.restype = i32
+        lib.mla_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+        lib.mla_decode_split_paged.restype = i32
         lib.mla_decode_merge.argtypes = [vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_merge.restype = i32
         lib.mla_decode_plan_destroy.argtypes = [vp]
@@ -120,10 +124,10 @@ def mla_status_string(status: int) -> str:
 
 
 def make_problem(batch_size, total_kv, q_dtype="bf16", kv_dtype="bf16", total_q=None, num_heads=16, qk_dim=576,
-                 v_dim=512, sm_scale=1.0 / 24.0, num_cus=0, max_q_len=0, logit_cap=0.0) -> mla_problem:
+                 v_dim=512, sm_scale=1.0 / 24.0, num_cus=0, max_q_len=0, logit_cap=0.0, kv_paged=0) -> mla_problem:
     return mla_problem(batch_size, batch_size if total_q is None else total_q, total_kv, num_heads, qk_dim, v_dim,
                        DTYPES.get(q_dtype, q_dtype), DTYPES.get(kv_dtype, kv_dtype), sm_scale, num_cus, max_q_len,
-                       logit_cap)
+                       logit_cap, int(kv_paged))
 
 
 class Plan:
@@ -173,6 +177,30 @@ def mla_decode_split(plan: Plan, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr,
                               _addr(kv_indptr), _addr(out), _addr(workspace), workspace_bytes, _stream(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_split")
+
+
+def mla_decode_run_paged(plan: Plan, q, q_scale, kv, kv_scale, kv_rows: int, kv_indices, qo_indptr, kv_indptr, out,
+                         workspace, workspace_bytes: int | None = None, stream=None) -> None:
+    lib = _lib_handle()
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    st = lib.mla_decode_run_paged(plan.handle, _addr(q), _addr(q_scale), _addr(kv), _addr(kv_scale), int(kv_rows),
+                                  _addr(kv_indices), _addr(qo_indptr), _addr(kv_indptr), _addr(out), _addr(workspace),
+                                  workspace_bytes, _stream(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_decode_run_paged")
+
+
+def mla_decode_split_paged(plan: Plan, q, q_scale, kv, kv_scale, kv_rows: int, kv_indices, qo_indptr, kv_indptr,
+                           out, workspace, workspace_bytes: int | None = None, stream=None) -> None:
+    lib = _lib_handle()
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    st = lib.mla_decode_split_paged(plan.handle, _addr(q), _addr(q_scale), _addr(kv), _addr(kv_scale), int(kv_rows),
+                                    _addr(kv_indices), _addr(qo_indptr), _addr(kv_indptr), _addr(out),
+                                    _addr(workspace), workspace_bytes, _stream(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_decode_split_paged")
 
 
 def mla_decode_merge(plan: Plan, qo_indptr, kv_indptr, out, workspace, workspace_bytes: int | None = None,

@@ -45,6 +45,7 @@
 
 #include <algorithm>
 #include <new>
+#include <type_traits>
 
 #include "mla_decode.h"
 
@@ -97,17 +98,26 @@ struct Geom {
   static constexpr int kRowBytes = kTile * kRow;       // row bytes of one tile
   static constexpr int kRowChunks = kRowBytes / 1024;  // one chunk = one wave DMA instruction
   static constexpr int kChunks = kRowChunks + KvGeom<KF>::kScaleChunks;
-  // DMA wave w issues chunks w, w + kDmaWaves, ...  For the 10-chunk MXFP4
-  // tile, leaving wave 3 out of the DMA (4/3/3 chunks) measured faster; the
-  // 18- and 36-chunk tiles spread over all four waves.
-  static constexpr int kDmaWaves = KvGeom<KF>::kDmaWaves;
-  static constexpr int kMaxChunksPerWave = (kChunks + kDmaWaves - 1) / kDmaWaves;
   static constexpr int kStageBytes = kChunks * 1024;
   static_assert(kRowBytes % 1024 == 0, "a tile must fill whole DMA chunks");
+};
+
+// Which waves move a tile.  DMA wave w issues chunks w, w + kWaves, ...  For the
+// 10-chunk MXFP4 tile, leaving wave 3 out of the DMA (4/3/3 chunks) measured
+// faster; the 18- and 36-chunk tiles spread over all four waves.  With paged KV
+// wave 3 stages the row indices instead and waves 0-2 move the rows.
+template <int KF, bool PAGED>
+struct Dma {
+  static constexpr int kWaves = PAGED ? 3 : KvGeom<KF>::kDmaWaves;
+  static constexpr int kMaxChunksPerWave = (Geom<KF>::kChunks + kWaves - 1) / kWaves;
   __host__ __device__ static constexpr int chunks_of_wave(int w) {
-    return w < kDmaWaves ? (kChunks - w + kDmaWaves - 1) / kDmaWaves : 0;
+    return w < kWaves ? (Geom<KF>::kChunks - w + kWaves - 1) / kWaves : 0;
   }
 };
+
+// Paged KV: the physical row indices of tile t sit in slot t % kIdxSlots of a
+// ring in LDS (32 int32 per slot), staged kIdxLead tiles ahead of need.
+constexpr int kIdxSlots = 8, kIdxLead = 3;
 
 // Partial-score exchange buffer of one query token, one plane per token of a
 // lane's f32x4: [wave][block][r][lane] floats, so the wave that finishes the
@@ -141,18 +151,30 @@ template <> struct RingCfg<DT_BF16, 4> { static constexpr int kStages = 3, kWgsP
 template <> struct RingCfg<DT_FP8, 4> { static constexpr int kStages = 6, kWgsPerCu = 1; };
 template <> struct RingCfg<DT_MXFP4, 4> { static constexpr int kStages = 8, kWgsPerCu = 1; };
 
+// Paged KV (bf16 and fp8 rows) adds the 1 KB index ring: fp8 keeps two
+// workgroups per CU with a three-slot ring, bf16 runs one with three slots.
 template <int KF, int QL>
+struct PagedRingCfg {
+  static constexpr int kStages = KF == DT_FP8 ? (QL == 4 ? 6 : 3) : 3;
+  static constexpr int kWgsPerCu = KF == DT_FP8 ? (QL == 4 ? 1 : 2) : 1;
+};
+
+template <int KF, int QL, bool PAGED>
 struct Ring {
-  static constexpr int kStages = RingCfg<KF, QL>::kStages;
-  static constexpr int kWgsPerCu = RingCfg<KF, QL>::kWgsPerCu;
+  using Cfg = std::conditional_t<PAGED, PagedRingCfg<KF, QL>, RingCfg<KF, QL>>;
+  static constexpr int kStages = Cfg::kStages;
+  static constexpr int kWgsPerCu = Cfg::kWgsPerCu;
   static constexpr int kLdsBytes = kStages * Geom<KF>::kStageBytes;
   static constexpr int kXchg = QL * kXchgBytes;
   static constexpr int kPBuf = 2 * (QL - 1) * kPTokBytes;
   static constexpr int kLut = KF == DT_MXFP4 ? 1024 : 0;  // E8M0 code -> fp32 table
-  static constexpr int kTotal = kLdsBytes + kXchg + kPBuf + kLut;
+  static constexpr int kIdx = PAGED ? kIdxSlots * kTile * 4 : 0;
+  static constexpr int kTotal = kLdsBytes + kXchg + kPBuf + kLut + kIdx;
   static_assert(kWgsPerCu * kTotal <= 160 * 1024, "resident workgroups per CU must fit the LDS");
-  static_assert((kStages - 2) * Geom<KF>::kMaxChunksPerWave <= 63, "vmcnt range");
+  static_assert((kStages - 2) * Dma<KF, PAGED>::kMaxChunksPerWave <= 63, "vmcnt range");
   static_assert(kStages >= 2 && kStages - 3 <= 5, "tiles behind the one needed near the end: 0..5");
+  static_assert(!PAGED || KF != DT_MXFP4, "paged KV: bf16 and fp8 rows");
+  static_assert(!PAGED || kIdxSlots >= kStages - 1 + kIdxLead, "index ring covers the tiles staged ahead");
 };
 
 // ------------------------------------------------------------ piece rules
@@ -295,6 +317,13 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // used for anything else in these kernels.
 __device__ inline void dma16(i32x4 r, uint32_t lds_base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// 4 bytes per active lane from rsrc + voff into LDS at lds_base + 4 * lane (the
+// paged-KV index staging; tracked with vmcnt like dma16).
+__device__ inline void dma4(i32x4 r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
                : "memory", "m0");
 }
 
@@ -520,6 +549,8 @@ struct SplitParams {
   int32_t rows_per_wg;
   float sm_scale;
   float logit_cap;  // > 0: scaled scores soft-capped as cap * tanh(s / cap)
+  const int32_t* kv_indices;  // paged KV: CSR row j is row kv_indices[j] of kv
+  int64_t kv_rows;            // paged KV: rows of the kv buffer
 };
 
 // Query operand of S^T = K Q^T for the dims this wave multiplies.  The four
@@ -1003,22 +1034,28 @@ __device__ inline void set_priority(int prio) {
 // One piece: rows [r0, r0 + n) of a sequence whose query rows are qrow0 ..
 // qrow0 + nq - 1 (nq in [1, QL]; the operands of tokens past nq repeat the
 // last row and their results are dropped).
-template <int QF, int KF, int QL, bool CAP>
-__device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf,
+template <int QF, int KF, int QL, bool CAP, bool PAGED>
+__device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf, int32_t* idxring,
                             const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow0, int nq, int64_t r0,
                             int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
   using G = Geom<KF>;
-  constexpr int NS = Ring<KF, QL>::kStages;
+  using DM = Dma<KF, PAGED>;
+  constexpr int NS = Ring<KF, QL, PAGED>::kStages;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int m = lane & 15;
   const int ntiles = (n + kTile - 1) / kTile;
 
-  // Buffer resources: rows from r0 on (reads past the buffer return zero).
-  const uint8_t* kv_base = p.kv + r0 * G::kRow;
-  const uint64_t kv_avail = (uint64_t)(p.total_kv - r0) * G::kRow;
+  // Buffer resources: rows from r0 on (reads past the buffer return zero); with
+  // paged KV the whole buffer (its size checked on the host) and the piece's
+  // indices.
+  const uint8_t* kv_base = PAGED ? p.kv : p.kv + r0 * G::kRow;
+  const uint64_t kv_avail = PAGED ? (uint64_t)p.kv_rows * G::kRow : (uint64_t)(p.total_kv - r0) * G::kRow;
   const i32x4 rk = make_rsrc(kv_base, (uint32_t)std::min<uint64_t>(kv_avail, 0xFFFFF000ull));
+  i32x4 ri = rk;
+  if constexpr (PAGED)
+    ri = make_rsrc(p.kv_indices + r0, (uint32_t)std::min<uint64_t>((uint64_t)(p.total_kv - r0) * 4, 0xFFFFF000ull));
   int64_t sbase = 0;
   i32x4 rs = rk;
   if constexpr (KF == DT_MXFP4) {
@@ -1027,22 +1064,31 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
     rs = make_rsrc(p.kv_scale + sbase, (uint32_t)std::min<uint64_t>(sbytes, 0xFFFFF000ull));
   }
 
-  // Tile t goes to slot t % NS; DMA wave w issues the chunks c = w, w + kDmaWaves, ...
-  // Lane offsets of its row chunks follow the swizzled layout.
-  uint32_t src[G::kMaxChunksPerWave];
+  // Tile t goes to slot t % NS; DMA wave w issues the chunks c = w, w + DM::kWaves, ...
+  // Lane offsets of its row chunks follow the swizzled layout: tile row prow[k],
+  // byte src[k] of the tile (of the row when paged).
+  uint32_t src[DM::kMaxChunksPerWave];
+  int prow[DM::kMaxChunksPerWave];
 #pragma unroll
-  for (int k = 0; k < G::kMaxChunksPerWave; ++k) {
-    const int c = w + G::kDmaWaves * k;
+  for (int k = 0; k < DM::kMaxChunksPerWave; ++k) {
+    const int c = w + DM::kWaves * k;
     src[k] = c < G::kRowChunks ? dma_src_offset<KF>(64 * c + lane) : 0u;
+    prow[k] = (int)(src[k] / G::kRow);
+    if (PAGED) src[k] -= (uint32_t)(prow[k] * G::kRow);
   }
   auto issue_tile = [&](int t) {
-    if (w >= G::kDmaWaves) return;
+    if (w >= DM::kWaves) return;
     const uint8_t* stage = ring + (t % NS) * G::kStageBytes;
+    const int32_t* ix = idxring + (t % kIdxSlots) * kTile;
 #pragma unroll
-    for (int k = 0; k < G::kMaxChunksPerWave; ++k) {
-      const int c = w + G::kDmaWaves * k;
+    for (int k = 0; k < DM::kMaxChunksPerWave; ++k) {
+      const int c = w + DM::kWaves * k;
       if (c >= G::kChunks) break;
-      if (c < G::kRowChunks) {
+      if (PAGED) {
+        // physical row of this lane's tile row (an index outside the buffer
+        // wraps or lands past its end, where the read returns zero)
+        dma16(rk, uniform(lds_addr(stage + c * 1024)), (uint32_t)ix[prow[k]] * (uint32_t)G::kRow + src[k]);
+      } else if (c < G::kRowChunks) {
         dma16(rk, uniform(lds_addr(stage + c * 1024)), (uint32_t)(t * G::kRowBytes) + src[k]);
       } else {
         const int64_t a = ((r0 + (int64_t)t * kTile) * kScaleRow) & ~(int64_t)15;
@@ -1055,11 +1101,25 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   lo.init(m, g, w);
   lo.e8m0 = e8m0_lut;
 
+  // Paged KV: wave 3 stages the physical row indices of tile t (32 lanes, 4
+  // bytes each) into index slot t % kIdxSlots, kIdxLead tiles ahead of the
+  // tile whose DMA needs them; waves 0-2 read them when they issue that DMA.
+  auto stage_idx = [&](int t) {
+    const uint32_t base = uniform(lds_addr(idxring + (t % kIdxSlots) * kTile));
+    if (lane < kTile) dma4(ri, base, (uint32_t)(t * kTile * 4) + 4 * lane);
+  };
+  if (PAGED && w == 3)
+    for (int t = 0; t <= NS - 2 + kIdxLead; ++t) stage_idx(t);
+
   QOperand<QF, KF> qop[QL];
 #pragma unroll
   for (int t = 0; t < QL; ++t) qop[t].fetch(p.q, qrow0 + std::min(t, nq - 1), lane, w);
 #pragma unroll
   for (int t = 0; t < QL; ++t) qop[t].arrive();
+  if constexpr (PAGED) {
+    if (w == 3) wait_vmcnt<0>();  // the staged indices are in LDS
+    lds_barrier();
+  }
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
   // per-token head maxima past the sequence counts at the start of xchg
@@ -1077,16 +1137,27 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
     for (int j = 0; j < 8; ++j) ws[t].acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int my_chunks = G::chunks_of_wave(w);
+  const int my_chunks = DM::chunks_of_wave(w);
   // tile i is complete in LDS and every wave is done with tile i - 1
   auto advance = [&](int i) {
     if (my_chunks > 0) {
       if (i + NS - 2 < ntiles)  // the usual case: the NS - 2 tiles after tile i stay in flight
-        wait_tiles_behind_fixed<G::kMaxChunksPerWave, NS - 2>(my_chunks);
+        wait_tiles_behind_fixed<DM::kMaxChunksPerWave, NS - 2>(my_chunks);
       else
-        wait_tiles_behind<G::kMaxChunksPerWave>(my_chunks, ntiles - 1 - i);
+        wait_tiles_behind<DM::kMaxChunksPerWave>(my_chunks, ntiles - 1 - i);
     }
     lds_barrier();
+  };
+  // Paged KV, after advance(i) of every tile with a refill: the indices of tile
+  // i + NS - 1 (staged kIdxLead steps earlier, or in the prologue) are complete
+  // for wave 3, and the score exchange barrier publishes them before refill(i)
+  // reads them; then the indices kIdxLead tiles further on go out.  Wave 3 has
+  // no other loads in flight, so vmcnt counts index loads only.
+  auto idx_step = [&](int i) {
+    if (PAGED && w == 3) {
+      wait_vmcnt<kIdxLead - 1>();
+      stage_idx(i + NS - 1 + kIdxLead);
+    }
   };
   // The DMA of tile i + NS - 1 (into the slot tile i - 1 left) goes out after
   // tile i's products are issued: when the memory pipeline is full the issue
@@ -1133,6 +1204,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   // tile 0, then for each later tile: its scores and the previous tile's products
   priority(0);
   advance(0);
+  idx_step(0);
   if (nfull > 0)
     score_tile<QF, KF, QL, CAP, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), kTile, cs, cap, ts);
   else
@@ -1142,6 +1214,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   for (int i = 1; i < nfull; ++i) {
     priority(i);
     advance(i);
+    idx_step(i);
     finish_tile<QF, KF, QL, false>(stage(i - 1), pbuf_of(i - 1), lo, ws, w, m, g, sdelta_of(i - 1), kTile, cs, ts);
     score_tile<QF, KF, QL, CAP, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile, cs, cap, ts);
     refill(i);
@@ -1160,6 +1233,8 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   else
     finish_tile<QF, KF, QL, false>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1),
                                    kTile, cs, ts);
+
+  if (PAGED && w == 3) wait_vmcnt<0>();  // no index load outlives the piece
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
   // running sums: this wave's rows (over the lane groups), then over the waves
@@ -1195,15 +1270,16 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   }
 }
 
-template <int QF, int KF, int QL, bool CAP>
+template <int QF, int KF, int QL, bool CAP, bool PAGED>
 __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(
-    Ring<KF, QL>::kWgsPerCu, Ring<KF, QL>::kWgsPerCu))) void mla_split_kernel(SplitParams p) {
+    Ring<KF, QL, PAGED>::kWgsPerCu, Ring<KF, QL, PAGED>::kWgsPerCu))) void mla_split_kernel(SplitParams p) {
   using G = Geom<KF>;
-  using RG = Ring<KF, QL>;
+  using RG = Ring<KF, QL, PAGED>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kLdsBytes];
   __shared__ float xchg[RG::kXchg / 4];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[QL > 1 ? RG::kPBuf : 16];
   __shared__ float e8m0_lut[KF == DT_MXFP4 ? 256 : 1];
+  __shared__ __attribute__((aligned(16))) int32_t idxring[PAGED ? kIdxSlots * kTile : 1];
   int* counts = (int*)xchg;  // the sequence search runs before any exchange
 
   const int tid = threadIdx.x;
@@ -1258,7 +1334,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
-    split_piece<QF, KF, QL, CAP>(p, ring, xchg, pbuf, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
+    split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
                             r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
     lds_barrier();  // the next piece refills the ring
   }
@@ -1452,22 +1528,23 @@ struct RingInfo {
   int stages, lds_bytes, wgs_per_cu;
 };
 
-template <int KF, int QL>
+template <int KF, int QL, bool PAGED>
 constexpr RingInfo ring_info() {
-  return RingInfo{Ring<KF, QL>::kStages, Ring<KF, QL>::kTotal, Ring<KF, QL>::kWgsPerCu};
+  return RingInfo{Ring<KF, QL, PAGED>::kStages, Ring<KF, QL, PAGED>::kTotal, Ring<KF, QL, PAGED>::kWgsPerCu};
 }
 
 template <int QL>
-RingInfo ring_info_for(int kv_dtype) {
+RingInfo ring_info_for(int kv_dtype, bool paged) {
   switch (kv_dtype) {
-    case DT_BF16: return ring_info<DT_BF16, QL>();
-    case DT_FP8: return ring_info<DT_FP8, QL>();
-    default: return ring_info<DT_MXFP4, QL>();
+    case DT_BF16: return paged ? ring_info<DT_BF16, QL, true>() : ring_info<DT_BF16, QL, false>();
+    case DT_FP8: return paged ? ring_info<DT_FP8, QL, true>() : ring_info<DT_FP8, QL, false>();
+    default: return ring_info<DT_MXFP4, QL, false>();  // paged MXFP4 is refused by the planner
   }
 }
 
-RingInfo ring_info_for(int kv_dtype, int ql) {
-  return ql == 1 ? ring_info_for<1>(kv_dtype) : ql == 2 ? ring_info_for<2>(kv_dtype) : ring_info_for<4>(kv_dtype);
+RingInfo ring_info_for(int kv_dtype, int ql, bool paged) {
+  return ql == 1 ? ring_info_for<1>(kv_dtype, paged)
+                 : ql == 2 ? ring_info_for<2>(kv_dtype, paged) : ring_info_for<4>(kv_dtype, paged);
 }
 
 // Smallest row range worth a workgroup: below it the partial write-back and the
@@ -1482,23 +1559,34 @@ int min_rows_for(int kv_dtype) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-template <int QF, int KF, bool CAP>
-void launch_split_cap(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
+template <int QF, int KF, bool CAP, bool PAGED>
+void launch_split_v(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
   const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads);
   if (pl->ql == 1)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED>), grid, block, 0, st, sp);
   else if (pl->ql == 2)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2, CAP>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2, CAP, PAGED>), grid, block, 0, st, sp);
   else
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4, CAP>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4, CAP, PAGED>), grid, block, 0, st, sp);
+}
+
+template <int QF, int KF, bool PAGED>
+void launch_split_p(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
+  if (pl->prob.logit_cap > 0.f)
+    launch_split_v<QF, KF, true, PAGED>(pl, sp, st);
+  else
+    launch_split_v<QF, KF, false, PAGED>(pl, sp, st);
 }
 
 template <int QF, int KF>
 hipError_t launch_split(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
-  if (pl->prob.logit_cap > 0.f)
-    launch_split_cap<QF, KF, true>(pl, sp, st);
-  else
-    launch_split_cap<QF, KF, false>(pl, sp, st);
+  if constexpr (KF != DT_MXFP4) {
+    if (pl->prob.kv_paged) {
+      launch_split_p<QF, KF, true>(pl, sp, st);
+      return hipGetLastError();
+    }
+  }
+  launch_split_p<QF, KF, false>(pl, sp, st);
   return hipGetLastError();
 }
 
@@ -1531,6 +1619,8 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   // query rows per sequence: one, or up to max_q_len (2 or 4 kernels; 3 runs on the 4-token one)
   if (pr->max_q_len < 0 || pr->max_q_len > 4) return MLA_ERR_UNSUPPORTED;
   if (!(pr->logit_cap >= 0.f) || !(pr->logit_cap < INFINITY)) return MLA_ERR_INVALID_ARG;
+  if (pr->kv_paged != 0 && pr->kv_paged != 1) return MLA_ERR_INVALID_ARG;
+  if (pr->kv_paged && pr->kv_dtype == DT_MXFP4) return MLA_ERR_UNSUPPORTED;
   const int ql = pr->max_q_len <= 1 ? 1 : pr->max_q_len == 2 ? 2 : 4;
   if (ql == 1 && pr->total_q != pr->batch_size) return MLA_ERR_UNSUPPORTED;  // one query token per sequence
   if (ql > 1 && (pr->total_q < 1 || (int64_t)pr->total_q > (int64_t)pr->batch_size * pr->max_q_len))
@@ -1554,7 +1644,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   }
 
   const int64_t total = pr->total_kv;
-  const RingInfo ri = ring_info_for(pr->kv_dtype, ql);
+  const RingInfo ri = ring_info_for(pr->kv_dtype, ql, pr->kv_paged != 0);
   const int wpc = (opt && opt->wgs_per_cu > 0) ? opt->wgs_per_cu : ri.wgs_per_cu;
   int64_t R;
   if (opt && opt->rows_per_split > 0) {
@@ -1678,11 +1768,19 @@ mla_status mla_decode_plan_merge_slots(const mla_plan* pl, const int32_t* ind, i
 namespace {
 
 // Validates the run arguments and fills the kernel parameter blocks.
+// kv_indices / kv_rows: the paged entry points (kv_indices != NULL) with a
+// paged plan, the others (NULL) with a contiguous one.
 mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, const void* kv, const void* kv_scale,
-                   const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
-                   size_t workspace_bytes, SplitParams* sp, MergeParams* mp) {
+                   const int32_t* kv_indices, int64_t kv_rows, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                   void* out, void* workspace, size_t workspace_bytes, SplitParams* sp, MergeParams* mp) {
   if (!pl || !q || !kv || !qo_indptr || !kv_indptr || !out) return MLA_ERR_INVALID_ARG;
   const mla_problem& pr = pl->prob;
+  if ((kv_indices != nullptr) != (pr.kv_paged != 0)) return MLA_ERR_INVALID_ARG;
+  if (kv_indices) {
+    const int64_t row_bytes = pr.kv_dtype == DT_BF16 ? 2 * kQK : kQK;
+    if (((uintptr_t)kv_indices & 3u) || kv_rows < 1) return MLA_ERR_INVALID_ARG;
+    if (kv_rows > (int64_t)0xFFFFF000 / row_bytes) return MLA_ERR_UNSUPPORTED;  // 32-bit row offsets
+  }
   if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
   if (pr.q_dtype == DT_FP8 && !q_scale) return MLA_ERR_INVALID_ARG;
   if (pr.kv_dtype != DT_BF16 && !kv_scale) return MLA_ERR_INVALID_ARG;
@@ -1704,6 +1802,8 @@ mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, cons
   sp->rows_per_wg = pl->rows_per_wg;
   sp->sm_scale = pr.sm_scale;
   sp->logit_cap = pr.logit_cap;
+  sp->kv_indices = kv_indices;
+  sp->kv_rows = kv_rows;
   mp->part_o = sp->part_o;
   mp->part_lse = sp->part_lse;
   mp->qo_indptr = qo_indptr;
@@ -1758,11 +1858,40 @@ mla_status mla_decode_run(const mla_plan* pl, const void* q, const float* q_scal
                           void* workspace, size_t workspace_bytes, void* stream) {
   SplitParams sp;
   MergeParams mp;
-  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, out, workspace, workspace_bytes, &sp, &mp);
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, nullptr, 0, qo_indptr, kv_indptr, out, workspace,
+                         workspace_bytes, &sp, &mp);
   if (s != MLA_OK) return s;
   s = launch_split_stage(pl, sp, (hipStream_t)stream);
   if (s != MLA_OK) return s;
   return launch_merge_stage(pl, mp, (hipStream_t)stream);
+}
+
+mla_status mla_decode_run_paged(const mla_plan* pl, const void* q, const float* q_scale, const void* kv,
+                                const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
+                                const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!kv_indices) return MLA_ERR_INVALID_ARG;
+  SplitParams sp;
+  MergeParams mp;
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, kv_indices, kv_rows, qo_indptr, kv_indptr, out, workspace,
+                         workspace_bytes, &sp, &mp);
+  if (s != MLA_OK) return s;
+  s = launch_split_stage(pl, sp, (hipStream_t)stream);
+  if (s != MLA_OK) return s;
+  return launch_merge_stage(pl, mp, (hipStream_t)stream);
+}
+
+mla_status mla_decode_split_paged(const mla_plan* pl, const void* q, const float* q_scale, const void* kv,
+                                  const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
+                                  const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!kv_indices) return MLA_ERR_INVALID_ARG;
+  SplitParams sp;
+  MergeParams mp;
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, kv_indices, kv_rows, qo_indptr, kv_indptr, out, workspace,
+                         workspace_bytes, &sp, &mp);
+  if (s != MLA_OK) return s;
+  return launch_split_stage(pl, sp, (hipStream_t)stream);
 }
 
 mla_status mla_decode_split(const mla_plan* pl, const void* q, const float* q_scale, const void* kv,
@@ -1770,7 +1899,8 @@ mla_status mla_decode_split(const mla_plan* pl, const void* q, const float* q_sc
                             void* workspace, size_t workspace_bytes, void* stream) {
   SplitParams sp;
   MergeParams mp;
-  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, out, workspace, workspace_bytes, &sp, &mp);
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, nullptr, 0, qo_indptr, kv_indptr, out, workspace,
+                         workspace_bytes, &sp, &mp);
   if (s != MLA_OK) return s;
   return launch_split_stage(pl, sp, (hipStream_t)stream);
 }

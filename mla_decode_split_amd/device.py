@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import (Plan, make_problem, mla_decode_merge, mla_decode_plan, mla_decode_plan_describe, mla_decode_run,
-               mla_decode_split, mla_plan_options)
+               mla_decode_run_paged, mla_decode_split, mla_decode_split_paged, mla_plan_options)
 
 
 @dataclass
@@ -26,6 +26,8 @@ class DeviceBatch:
     kv_indptr_host: np.ndarray
     max_q_len: int
     logit_cap: float
+    kv_indices: torch.Tensor | None  # paged KV (page size 1): CSR row j is kv row kv_indices[j]
+    total_kv_rows: int               # CSR rows (kv rows when not paged)
     q_dtype: str
     kv_dtype: str
     sm_scale: float
@@ -40,6 +42,10 @@ class DeviceBatch:
 
     @property
     def total_kv(self) -> int:
+        return self.total_kv_rows
+
+    @property
+    def kv_rows(self) -> int:
         return int(self.kv.shape[0])
 
 
@@ -67,6 +73,9 @@ def upload(w, device="cuda") -> DeviceBatch:
                        kv_indptr_host=np.ascontiguousarray(w.kv_indptr, dtype=np.int32),
                        max_q_len=int(np.diff(np.asarray(w.qo_indptr, dtype=np.int64)).max(initial=0)),
                        logit_cap=float(getattr(w, "logit_cap", 0.0)),
+                       kv_indices=None if getattr(w, "kv_indices", None) is None
+                       else _to_dev(np.asarray(w.kv_indices, dtype=np.int32), device),
+                       total_kv_rows=int(w.total_kv),
                        q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, sm_scale=float(w.sm_scale))
 
 
@@ -74,7 +83,7 @@ def plan_for(batch: DeviceBatch, rows_per_split: int = 0, wgs_per_cu: int = 0, u
              num_cus: int = 0) -> Plan:
     prob = make_problem(batch.batch_size, batch.total_kv, batch.q_dtype, batch.kv_dtype, total_q=batch.total_q,
                         sm_scale=batch.sm_scale, num_cus=num_cus, max_q_len=batch.max_q_len,
-                        logit_cap=batch.logit_cap)
+                        logit_cap=batch.logit_cap, kv_paged=batch.kv_indices is not None)
     opts = mla_plan_options(rows_per_split, wgs_per_cu) if (rows_per_split or wgs_per_cu) else None
     return mla_decode_plan(prob, opts, batch.kv_indptr_host if use_host_indptr else None)
 
@@ -93,14 +102,23 @@ def run(plan: Plan, batch: DeviceBatch, out: torch.Tensor | None = None, workspa
         out = torch.empty((batch.total_q, 16, 512), dtype=torch.bfloat16, device=batch.q.device)
     if workspace is None:
         workspace = workspace_for(plan, batch.q.device)
-    mla_decode_run(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.qo_indptr, batch.kv_indptr, out,
-                   workspace, workspace.numel(), stream)
+    if batch.kv_indices is not None:
+        mla_decode_run_paged(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.kv_rows, batch.kv_indices,
+                             batch.qo_indptr, batch.kv_indptr, out, workspace, workspace.numel(), stream)
+    else:
+        mla_decode_run(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.qo_indptr, batch.kv_indptr, out,
+                       workspace, workspace.numel(), stream)
     return out
 
 
 def run_split(plan: Plan, batch: DeviceBatch, out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
-    mla_decode_split(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.qo_indptr, batch.kv_indptr, out,
-                     workspace, workspace.numel(), stream)
+    if batch.kv_indices is not None:
+        mla_decode_split_paged(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.kv_rows,
+                               batch.kv_indices, batch.qo_indptr, batch.kv_indptr, out, workspace, workspace.numel(),
+                               stream)
+    else:
+        mla_decode_split(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.qo_indptr, batch.kv_indptr,
+                         out, workspace, workspace.numel(), stream)
 
 
 def run_merge(plan: Plan, batch: DeviceBatch, out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:

@@ -234,5 +234,43 @@ def test_run_argument_errors_before_any_launch():
     assert mla.library().mla_debug_stream_read(A, 0, A, None) == mla.MLA_OK                 # nothing to launch
 
 
+@pytest.mark.parametrize("kv_dtype,q_len", [("fp8", 1), ("fp8", 2), ("fp8", 4), ("bf16", 1), ("bf16", 2)])
+def test_paged_plans(kv_dtype, q_len):
+    ind = _indptr([8192] * 64)
+    prob = mla.make_problem(64, int(ind[-1]), "bf16", kv_dtype, total_q=64 * q_len, num_cus=256, max_q_len=q_len,
+                            kv_paged=1)
+    plan = mla.mla_decode_plan(prob, None, ind)
+    d = mla.mla_decode_plan_describe(plan)
+    assert d["lds_bytes"] * d["wgs_per_cu"] <= 160 * 1024
+    if kv_dtype == "fp8" and q_len < 4:
+        assert d["wgs_per_cu"] == 2  # the index ring still leaves room for two workgroups
+    _check_cut(plan, ind)
+
+
+def test_paged_argument_errors_before_any_launch():
+    """Every call below fails host-side validation (fake, never dereferenced addresses)."""
+    prob = mla.make_problem(4, 100, num_cus=256, kv_dtype="mxfp4", kv_paged=1)
+    assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_UNSUPPORTED  # paged MXFP4
+    prob = mla.make_problem(4, 100, num_cus=256, kv_paged=2)
+    assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG
+    A = 1 << 20
+    ind = _indptr([32, 32])
+    flat = _plan(2, 64, kv="fp8", ind=ind)
+    paged = mla.mla_decode_plan(mla.make_problem(2, 64, "bf16", "fp8", num_cus=256, kv_paged=1), None, ind)
+    n = paged.workspace_bytes
+
+    def run_paged(plan, kv_rows=1000, kv_indices=A):
+        return _status(mla.mla_decode_run_paged, plan, A, A, A, A, kv_rows, kv_indices, A, A, A, A, n)
+
+    assert run_paged(flat) == mla.MLA_ERR_INVALID_ARG                    # contiguous plan
+    assert run_paged(paged, kv_indices=None) == mla.MLA_ERR_INVALID_ARG
+    assert run_paged(paged, kv_indices=A + 2) == mla.MLA_ERR_INVALID_ARG  # not 4-byte aligned
+    assert run_paged(paged, kv_rows=0) == mla.MLA_ERR_INVALID_ARG
+    assert run_paged(paged, kv_rows=1 << 23) == mla.MLA_ERR_UNSUPPORTED   # > 4 GB of fp8 rows
+    assert _status(mla.mla_decode_run, paged, A, A, A, A, A, A, A, A, n) == mla.MLA_ERR_INVALID_ARG
+    assert _status(mla.mla_decode_split, paged, A, A, A, A, A, A, A, A, n) == mla.MLA_ERR_INVALID_ARG
+    assert _status(mla.mla_decode_split_paged, flat, A, A, A, A, 1000, A, A, A, A, A, n) == mla.MLA_ERR_INVALID_ARG
+
+
 def test_plan_destroy_accepts_null():
     mla.library().mla_decode_plan_destroy(None)

@@ -258,6 +258,58 @@ def test_soft_cap_saturating_scores():
     _check_batch(w, rows_per_split=256, what="logit_cap 4, saturating scores")
 
 
+# ------------------------------------------------------------- paged KV (page size 1)
+
+PAGED_COMBOS = [c for c in COMBOS if c[1] != "mxfp4"]
+
+
+def _paged_equals_contiguous(w, pw, rows_per_split=0, what=""):
+    """The paged run reads the same CSR rows as the contiguous one, through the
+    indices: the outputs agree bit for bit."""
+    b, pb = dev.upload(w), dev.upload(pw)
+    o1 = dev.run(dev.plan_for(b, rows_per_split=rows_per_split), b)
+    o2 = dev.run(dev.plan_for(pb, rows_per_split=rows_per_split), pb)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o1.view(torch.int16), o2.view(torch.int16)))
+    _say(f"{what}: paged == contiguous bitwise: {same}")
+    assert same
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", PAGED_COMBOS)
+def test_paged_edge_lengths(q_dtype, kv_dtype):
+    w = synth.make_batch(EDGE_LENGTHS, q_dtype, kv_dtype, seed=151, name="paged-edges")
+    pw = synth.page_workload(w, seed=152, spare_rows=777)
+    _check_batch(pw, what=f"paged {q_dtype}/{kv_dtype}")
+    _paged_equals_contiguous(w, pw, what=f"paged {q_dtype}/{kv_dtype}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("rows", [32, 96, 512])
+def test_paged_query_rows_cap_and_splits(kv_dtype, rows):
+    w = synth.make_batch([700, 0, 33, 1000, 1, 257], "bf16", kv_dtype, seed=161, name="paged-mix",
+                         q_lens=[2, 1, 4, 0, 3, 1])
+    w.logit_cap = 2.0
+    pw = synth.page_workload(w, seed=162, spare_rows=100)
+    _check_batch(pw, rows_per_split=rows, what=f"paged, q rows <= 4, cap 2, rows_per_split={rows} kv={kv_dtype}")
+    _paged_equals_contiguous(w, pw, rows_per_split=rows, what=f"paged mix rows={rows} kv={kv_dtype}")
+
+
+def test_paged_plan_without_host_indptr():
+    w = synth.make_batch([100, 7, 900, 64], "bf16", "fp8", seed=171, name="paged-no-host")
+    pw = synth.page_workload(w, seed=172, spare_rows=64)
+    _check_batch(pw, use_host_indptr=False, rows_per_split=128, what="paged, plan without host indptr")
+
+
+def test_paged_full_size_sampled():
+    # bs 64, KV 8192 fp8 scattered over a buffer with 1/8 spare rows, in the
+    # planner's launch configuration: sampled sequences against the oracle, the
+    # whole output bitwise against the contiguous run
+    w = synth.make_workload("bs64_kv8192_fp8")
+    pw = synth.page_workload(w, seed=181, spare_rows=w.total_kv // 8)
+    _check_batch(pw, seq_ids=[0, 1, 31, 63], poison=False, what="bs64 kv8192 fp8 paged (sampled)")
+    _paged_equals_contiguous(w, pw, what="bs64 kv8192 fp8 paged")
+
+
 def test_runs_are_deterministic():
     w = synth.make_batch([3000, 17, 4000], "bf16", "fp8", seed=707, name="det")
     b = dev.upload(w)
