@@ -36,6 +36,17 @@
 //        V^T gathered from the same LDS tile, P^T read back from LDS.
 // A tile costs two workgroup barriers: tile i's scores, then - after the next
 // ring barrier - tile i-1's products.
+//
+// Variants (template parameters of the stage-1 kernel):
+//   QL    query rows per sequence held together (1, 2, 4): every KV tile is
+//         multiplied with all of them (multi-token prediction, speculative
+//         decoding), one exchange plane and one accumulator set per row;
+//   CAP   scaled scores soft-capped as cap * tanh(s / cap) before the softmax
+//         (the logit_cap argument of the library call on submission 753817's
+//         page, which passes 0.0);
+//   PAGED page size 1: CSR row j is row kv_indices[j] of the buffer (the
+//         kv_indices / page_size 1 layout of that call); wave 3 stages each
+//         tile's row indices in LDS, waves 0-2 gather the rows.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
