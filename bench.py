@@ -43,9 +43,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "4128f425e775a4effae67ed9db74936e5e7ae2a42ad00e957421e6b9c15eebe2",
-    "fetch_kib": 152177.8,
-    "write_kib": 8224.1,
+    "source_sha256": "eb2c1bd7f09b89fc621d0ddf05923e835f567351541d794967ec27b781356dd9",
+    "fetch_kib": 152176.8,
+    "write_kib": 8224.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
