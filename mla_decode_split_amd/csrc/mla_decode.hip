@@ -40,7 +40,8 @@
 // Variants (template parameters of the stage-1 kernel):
 //   QL    query rows per sequence held together (1, 2, 4): every KV tile is
 //         multiplied with all of them (multi-token prediction, speculative
-//         decoding), one exchange plane and one accumulator set per row;
+//         decoding), one exchange plane and one accumulator set per row; four
+//         rows run as two groups of four waves, two rows each, over one ring;
 //   CAP   scaled scores soft-capped as cap * tanh(s / cap) before the softmax
 //         (the logit_cap argument of the library call on submission 753817's
 //         page, which passes 0.0);
@@ -138,6 +139,15 @@ constexpr int kXchgBytes = 4 * 2 * 4 * 64 * 4;
 // bytes): the bf16 P of every lane (16 bytes each) and the four waves' maxima
 // of every head (16 bytes each), per tile parity.
 constexpr int kPTokBytes = 64 * 16 + kHeads * 16;
+
+// Query rows per wave and 4-wave groups per workgroup.  With four rows, two
+// groups of four waves take two rows each over one shared ring, so each wave
+// carries the registers of two rows and each SIMD runs two waves.
+template <int QL>
+struct RowSplit {
+  static constexpr int kGroups = QL == 4 ? 2 : 1;
+  static constexpr int kPerWave = QL / kGroups;
+};
 
 // Ring depth and residency per (KV format, query tokens per sequence QL).  Each
 // query token adds its score-exchange plane, its probability buffers and ~60
@@ -881,12 +891,13 @@ __device__ inline int max_slot(int h) {
   else  // E2M1 rows have two rope units: the unused tail of the tile's scale chunk
     return Geom<KF>::kRowBytes + 768 + 16 * h;
 }
+// flag words of waves 4 * half .. 4 * half + 3 (half 1 only with two row groups)
 template <int KF>
-__device__ inline int flag_slot() {
+__device__ inline int flag_slot(int half) {
   if constexpr (RopeUnits<KF>::kCount >= 4)
-    return 16 * ((RopeUnits<KF>::kFirst + 3) ^ Layout<KF>::swz(0));
+    return half * Geom<KF>::kRow + 16 * ((RopeUnits<KF>::kFirst + 3) ^ Layout<KF>::swz(half));
   else
-    return Geom<KF>::kRowBytes + 704;
+    return Geom<KF>::kRowBytes + 704 + 16 * half;
 }
 
 // P slot and max slot of query token t: token 0 in the tile's rope bytes, later
@@ -939,26 +950,30 @@ struct TileScores {
   float p[2];   // their probabilities against m_run as it was when they were posted
 };
 
-template <int QF, int KF, int QL, bool CAP, bool MASK>
-__device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const QOperand<QF, KF> (&qo)[QL],
-                                  const LaneOffs<KF>& lo, const WaveState (&ws)[QL], int w, int m, int g, int sdelta,
-                                  int valid, const float (&c)[QL], const SoftCap<QL, CAP>& cap, TileScores (&ts)[QL]) {
+// tb: the first query row of this wave's group; w8: the wave in the workgroup
+// (w = w8 & 3 its share of dims and value columns).
+template <int QF, int KF, int QW, int NG, bool CAP, bool MASK>
+__device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const QOperand<QF, KF> (&qo)[QW],
+                                  const LaneOffs<KF>& lo, const WaveState (&ws)[QW], int w, int w8, int tb, int m, int g,
+                                  int sdelta, int valid, const float (&c)[QW], const SoftCap<QW, CAP>& cap,
+                                  TileScores (&ts)[QW]) {
   const int lane = threadIdx.x & 63;
   {
-    f32x4 part[QL][2];
-    qk_tile<QF, KF, QL>(st, qo, lo, w, m, sdelta, part);
+    f32x4 part[QW][2];
+    qk_tile<QF, KF, QW>(st, qo, lo, w, m, sdelta, part);
 #pragma unroll
-    for (int t = 0; t < QL; ++t)
+    for (int t = 0; t < QW; ++t)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xchg[t * (kXchgBytes / 4) + ((2 * w + blk) * 4 + r) * 64 + lane] = part[t][blk][r];
+        for (int r = 0; r < 4; ++r)
+          xchg[(tb + t) * (kXchgBytes / 4) + ((2 * w + blk) * 4 + r) * 64 + lane] = part[t][blk][r];
   }
   lds_barrier();  // every wave's partial scores are in LDS and every wave is done with the rope dims
   int flags = 0;
 #pragma unroll
-  for (int t = 0; t < QL; ++t) {
-    const float* xt = xchg + t * (kXchgBytes / 4);
+  for (int t = 0; t < QW; ++t) {
+    const float* xt = xchg + (tb + t) * (kXchgBytes / 4);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       // summed in wave order
@@ -973,37 +988,47 @@ __device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const Q
     const float t0 = fmaf(ts[t].sv[0], c[t], -ws[t].m_run), t1 = fmaf(ts[t].sv[1], c[t], -ws[t].m_run);
     ts[t].p[0] = __builtin_amdgcn_exp2f(t0);
     ts[t].p[1] = __builtin_amdgcn_exp2f(t1);
-    uint8_t* ps = p_ptr<KF>(st, pb, t, lane);
+    uint8_t* ps = p_ptr<KF>(st, pb, tb + t, lane);
     *(__bf16*)(ps + 2 * w) = (__bf16)ts[t].p[0];
     *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts[t].p[1];
-    if (__builtin_amdgcn_ballot_w64(t0 > kRescaleSlack || t1 > kRescaleSlack) != 0) flags |= 1 << t;
+    if (__builtin_amdgcn_ballot_w64(t0 > kRescaleSlack || t1 > kRescaleSlack) != 0) flags |= 1 << (tb + t);
   }
-  if (lane == 0) ((int*)(st + flag_slot<KF>()))[w] = flags;
+  if (lane == 0) {
+    if constexpr (NG == 1)
+      ((int*)(st + flag_slot<KF>(0)))[w] = flags;
+    else
+      ((int*)(st + flag_slot<KF>(w8 >> 2)))[w8 & 3] = flags;
+  }
 }
 
-template <int QF, int KF, int QL, bool MASK>
-__device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>& lo, WaveState (&ws)[QL], int w, int m,
-                                   int g, int sdelta, int valid, const float (&c)[QL], TileScores (&ts)[QL]) {
+template <int QF, int KF, int QW, int NG, bool MASK>
+__device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>& lo, WaveState (&ws)[QW], int w, int tb,
+                                   int m, int g, int sdelta, int valid, const float (&c)[QW], TileScores (&ts)[QW]) {
   const int lane = threadIdx.x & 63;
   bf16x8 va[8];
   load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
-  const u32x4 fl = *(const u32x4*)(st + flag_slot<KF>());
-  const uint32_t any = fl[0] | fl[1] | fl[2] | fl[3];
+  // bit r: some wave flagged query row r (the same value in every wave)
+  const u32x4 fl = *(const u32x4*)(st + flag_slot<KF>(0));
+  uint32_t any = fl[0] | fl[1] | fl[2] | fl[3];
+  if constexpr (NG == 2) {
+    const u32x4 f1 = *(const u32x4*)(st + flag_slot<KF>(1));
+    any |= f1[0] | f1[1] | f1[2] | f1[3];
+  }
   if (any != 0u) {
 #pragma unroll
-    for (int t = 0; t < QL; ++t) {
-      if (!((any >> t) & 1u)) continue;
+    for (int t = 0; t < QW; ++t) {
+      if (!((any >> (tb + t)) & 1u)) continue;
       // tile maximum per head: this wave's rows (over the lane groups), then the waves
       float mx = fmaxf(ts[t].sv[0], ts[t].sv[1]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      if (g == 0) *(float*)(max_ptr<KF>(st, pb, t, m) + 4 * w) = mx * c[t];
+      if (g == 0) *(float*)(max_ptr<KF>(st, pb, tb + t, m) + 4 * w) = mx * c[t];
     }
     lds_barrier();
 #pragma unroll
-    for (int t = 0; t < QL; ++t) {
-      if (!((any >> t) & 1u)) continue;
-      const f32x4 mw = *(const f32x4*)max_ptr<KF>(st, pb, t, m);
+    for (int t = 0; t < QW; ++t) {
+      if (!((any >> (tb + t)) & 1u)) continue;
+      const f32x4 mw = *(const f32x4*)max_ptr<KF>(st, pb, tb + t, m);
       const float tmax = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
       const float m_new = fmaxf(ws[t].m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(ws[t].m_run - m_new);
@@ -1013,16 +1038,16 @@ __device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>&
       for (int j = 0; j < 8; ++j) ws[t].acc[j] *= alpha;
       ts[t].p[0] = __builtin_amdgcn_exp2f(fmaf(ts[t].sv[0], c[t], -ws[t].m_run));
       ts[t].p[1] = __builtin_amdgcn_exp2f(fmaf(ts[t].sv[1], c[t], -ws[t].m_run));
-      uint8_t* ps = p_ptr<KF>(st, pb, t, lane);
+      uint8_t* ps = p_ptr<KF>(st, pb, tb + t, lane);
       *(__bf16*)(ps + 2 * w) = (__bf16)ts[t].p[0];
       *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts[t].p[1];
     }
     lds_barrier();  // the probabilities against the new maxima are in LDS
   }
 #pragma unroll
-  for (int t = 0; t < QL; ++t) {
+  for (int t = 0; t < QW; ++t) {
     ws[t].l_run += ts[t].p[0] + ts[t].p[1];
-    const bf16x8 pv = __builtin_bit_cast(bf16x8, *(const u32x4*)p_ptr<KF>(st, pb, t, lane));
+    const bf16x8 pv = __builtin_bit_cast(bf16x8, *(const u32x4*)p_ptr<KF>(st, pb, tb + t, lane));
 #pragma unroll
     for (int j = 0; j < 8; ++j) ws[t].acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pv, ws[t].acc[j], 0, 0, 0);
   }
@@ -1052,8 +1077,13 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   using G = Geom<KF>;
   using DM = Dma<KF, PAGED>;
   constexpr int NS = Ring<KF, QL, PAGED>::kStages;
+  constexpr int NG = RowSplit<QL>::kGroups, QW = RowSplit<QL>::kPerWave;
   const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
+  const int w8 = uniform(threadIdx.x >> 6);
+  const int w = NG == 1 ? w8 : (w8 & 3);      // share of dims and value columns
+  const int grp = NG == 1 ? 0 : (w8 >> 2);    // row group: query rows tb .. tb + QW - 1
+  const int tb = grp * QW;
+  const int wd = grp == 0 ? w : Geom<KF>::kWaves;  // DMA wave index (group 0 moves the tiles)
   const int g = lane >> 4;
   const int m = lane & 15;
   const int ntiles = (n + kTile - 1) / kTile;
@@ -1082,18 +1112,18 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   int prow[DM::kMaxChunksPerWave];
 #pragma unroll
   for (int k = 0; k < DM::kMaxChunksPerWave; ++k) {
-    const int c = w + DM::kWaves * k;
+    const int c = wd + DM::kWaves * k;
     src[k] = c < G::kRowChunks ? dma_src_offset<KF>(64 * c + lane) : 0u;
     prow[k] = (int)(src[k] / G::kRow);
     if (PAGED) src[k] -= (uint32_t)(prow[k] * G::kRow);
   }
   auto issue_tile = [&](int t) {
-    if (w >= DM::kWaves) return;
+    if (wd >= DM::kWaves) return;
     const uint8_t* stage = ring + (t % NS) * G::kStageBytes;
     const int32_t* ix = idxring + (t % kIdxSlots) * kTile;
 #pragma unroll
     for (int k = 0; k < DM::kMaxChunksPerWave; ++k) {
-      const int c = w + DM::kWaves * k;
+      const int c = wd + DM::kWaves * k;
       if (c >= G::kChunks) break;
       if (PAGED) {
         // physical row of this lane's tile row (an index outside the buffer
@@ -1119,36 +1149,36 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
     const uint32_t base = uniform(lds_addr(idxring + (t % kIdxSlots) * kTile));
     if (lane < kTile) dma4(ri, base, (uint32_t)(t * kTile * 4) + 4 * lane);
   };
-  if (PAGED && w == 3)
+  if (PAGED && wd == 3)
     for (int t = 0; t <= NS - 2 + kIdxLead; ++t) stage_idx(t);
 
-  QOperand<QF, KF> qop[QL];
+  QOperand<QF, KF> qop[QW];
 #pragma unroll
-  for (int t = 0; t < QL; ++t) qop[t].fetch(p.q, qrow0 + std::min(t, nq - 1), lane, w);
+  for (int t = 0; t < QW; ++t) qop[t].fetch(p.q, qrow0 + std::min(tb + t, nq - 1), lane, w);
 #pragma unroll
-  for (int t = 0; t < QL; ++t) qop[t].arrive();
+  for (int t = 0; t < QW; ++t) qop[t].arrive();
   if constexpr (PAGED) {
-    if (w == 3) wait_vmcnt<0>();  // the staged indices are in LDS
+    if (wd == 3) wait_vmcnt<0>();  // the staged indices are in LDS
     lds_barrier();
   }
   const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
   // per-token head maxima past the sequence counts at the start of xchg
 #pragma unroll
-  for (int t = 0; t < QL; ++t) qop[t].prepare(xchg + 256 + 64 * t, w, lane);
+  for (int t = 0; t < QW; ++t) qop[t].prepare(xchg + 256 + 64 * (tb + t), w, lane);
 #pragma unroll
-  for (int t = 0; t < QL; ++t) qop[t].settle();
+  for (int t = 0; t < QW; ++t) qop[t].settle();
 
-  WaveState ws[QL];
+  WaveState ws[QW];
 #pragma unroll
-  for (int t = 0; t < QL; ++t) {
+  for (int t = 0; t < QW; ++t) {
     ws[t].m_run = -INFINITY;
     ws[t].l_run = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ws[t].acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int my_chunks = DM::chunks_of_wave(w);
+  const int my_chunks = DM::chunks_of_wave(wd);
   // tile i is complete in LDS and every wave is done with tile i - 1
   auto advance = [&](int i) {
     if (my_chunks > 0) {
@@ -1165,7 +1195,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   // reads them; then the indices kIdxLead tiles further on go out.  Wave 3 has
   // no other loads in flight, so vmcnt counts index loads only.
   auto idx_step = [&](int i) {
-    if (PAGED && w == 3) {
+    if (PAGED && wd == 3) {
       wait_vmcnt<kIdxLead - 1>();
       stage_idx(i + NS - 1 + kIdxLead);
     }
@@ -1196,12 +1226,12 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
       set_priority(prio);
     }
   };
-  float cs[QL];
+  float cs[QW];
 #pragma unroll
-  for (int t = 0; t < QL; ++t) cs[t] = score_scale * qop[t].scale;
-  SoftCap<QL, CAP> cap;
+  for (int t = 0; t < QW; ++t) cs[t] = score_scale * qop[t].scale;
+  SoftCap<QW, CAP> cap;
 #pragma unroll
-  for (int t = 0; t < QL; ++t) {
+  for (int t = 0; t < QW; ++t) {
     // c = 0 (a zero q or KV scale): every score is 0 and stays 0
     const bool live = CAP && cs[t] > 0.f;
     cap.u[t] = live ? p.logit_cap * kLog2e / cs[t] : 0.f;
@@ -1211,63 +1241,64 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   auto stage = [&](int i) { return ring + (i % NS) * G::kStageBytes; };
   // probability records of tokens >= 1: one set per tile parity
   auto pbuf_of = [&](int i) { return pbuf + (i & 1) * ((QL - 1) * kPTokBytes); };
-  TileScores ts[QL];
+  TileScores ts[QW];
   // tile 0, then for each later tile: its scores and the previous tile's products
   priority(0);
   advance(0);
   idx_step(0);
   if (nfull > 0)
-    score_tile<QF, KF, QL, CAP, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), kTile, cs, cap, ts);
+    score_tile<QF, KF, QW, NG, CAP, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(0), kTile, cs, cap, ts);
   else
-    score_tile<QF, KF, QL, CAP, true>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, m, g, sdelta_of(0), last_valid, cs, cap,
+    score_tile<QF, KF, QW, NG, CAP, true>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(0), last_valid, cs, cap,
                                  ts);
   refill(0);
   for (int i = 1; i < nfull; ++i) {
     priority(i);
     advance(i);
     idx_step(i);
-    finish_tile<QF, KF, QL, false>(stage(i - 1), pbuf_of(i - 1), lo, ws, w, m, g, sdelta_of(i - 1), kTile, cs, ts);
-    score_tile<QF, KF, QL, CAP, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, m, g, sdelta_of(i), kTile, cs, cap, ts);
+    finish_tile<QF, KF, QW, NG, false>(stage(i - 1), pbuf_of(i - 1), lo, ws, w, tb, m, g, sdelta_of(i - 1), kTile, cs, ts);
+    score_tile<QF, KF, QW, NG, CAP, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(i), kTile, cs, cap, ts);
     refill(i);
   }
   if (nfull > 0 && nfull < ntiles) {  // the partial last tile
     advance(nfull);
-    finish_tile<QF, KF, QL, false>(stage(nfull - 1), pbuf_of(nfull - 1), lo, ws, w, m, g, sdelta_of(nfull - 1), kTile,
+    finish_tile<QF, KF, QW, NG, false>(stage(nfull - 1), pbuf_of(nfull - 1), lo, ws, w, tb, m, g, sdelta_of(nfull - 1), kTile,
                                    cs, ts);
-    score_tile<QF, KF, QL, CAP, true>(stage(nfull), pbuf_of(nfull), xchg, qop, lo, ws, w, m, g, sdelta_of(nfull),
+    score_tile<QF, KF, QW, NG, CAP, true>(stage(nfull), pbuf_of(nfull), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(nfull),
                                  last_valid, cs, cap, ts);
   }
   lds_barrier();  // the last tile's probabilities are in LDS
   if (nfull < ntiles)
-    finish_tile<QF, KF, QL, true>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1),
+    finish_tile<QF, KF, QW, NG, true>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, tb, m, g, sdelta_of(ntiles - 1),
                                   last_valid, cs, ts);
   else
-    finish_tile<QF, KF, QL, false>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, m, g, sdelta_of(ntiles - 1),
+    finish_tile<QF, KF, QW, NG, false>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, tb, m, g, sdelta_of(ntiles - 1),
                                    kTile, cs, ts);
 
-  if (PAGED && w == 3) wait_vmcnt<0>();  // no index load outlives the piece
+  if (PAGED && wd == 3) wait_vmcnt<0>();  // no index load outlives the piece
 
   // ---- epilogue: lane (head m, group g) holds columns 128w + 32g + 8r + j in acc[j][r]
   // running sums: this wave's rows (over the lane groups), then over the waves
   // (every wave is past its last read of the score planes)
-  float lt[QL];
+  float lt[QW];
 #pragma unroll
-  for (int t = 0; t < QL; ++t) {
+  for (int t = 0; t < QW; ++t) {
     lt[t] = ws[t].l_run + shfl_xor(ws[t].l_run, 16);
     lt[t] += shfl_xor(lt[t], 32);
-    if (g == 0) xchg[64 * t + 16 * w + m] = lt[t];
+    if (g == 0) xchg[64 * (tb + t) + 16 * w + m] = lt[t];
   }
   lds_barrier();
   const int col0 = 128 * w + 32 * g;
 #pragma unroll
-  for (int t = 0; t < QL; ++t) {
-    if (t >= nq) break;
-    lt[t] = xchg[64 * t + m] + xchg[64 * t + 16 + m] + xchg[64 * t + 32 + m] + xchg[64 * t + 48 + m];
+  for (int t = 0; t < QW; ++t) {
+    const int r = tb + t;  // query row of the sequence
+    if (r >= nq) break;
+    lt[t] = xchg[64 * r + m] + xchg[64 * r + 16 + m] + xchg[64 * r + 32 + m] + xchg[64 * r + 48 + m];
     const float inv = out_scale / lt[t];
     // whole sequence: the output; piece of a split one: its partial O, also bf16 (the
     // merge adds at most one bf16 rounding of the weighted terms to the output's own)
-    uint16_t* o = (slot < 0 ? p.out + ((qrow0 + t) * kHeads + m) * kV
-                            : p.part_o + (((int64_t)slot * QL + t) * kHeads + m) * kV) +
+    uint16_t* o = (slot < 0 ? p.out + ((qrow0 + r) * kHeads + m) * kV
+                            : p.part_o + (((int64_t)slot * QL + r) * kHeads + m) * kV) +
                   col0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1277,15 +1308,16 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
       *(u32x4*)(o + 8 * r) = v;
     }
     if (slot >= 0 && w == 0 && g == 0)
-      p.part_lse[((int64_t)slot * QL + t) * kHeads + m] = (ws[t].m_run + __builtin_amdgcn_logf(lt[t])) * kLn2;
+      p.part_lse[((int64_t)slot * QL + r) * kHeads + m] = (ws[t].m_run + __builtin_amdgcn_logf(lt[t])) * kLn2;
   }
 }
 
 template <int QF, int KF, int QL, bool CAP, bool PAGED>
-__global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per_eu(
-    Ring<KF, QL, PAGED>::kWgsPerCu, Ring<KF, QL, PAGED>::kWgsPerCu))) void mla_split_kernel(SplitParams p) {
-  using G = Geom<KF>;
+__global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attribute__((amdgpu_waves_per_eu(
+    Ring<KF, QL, PAGED>::kWgsPerCu * RowSplit<QL>::kGroups,
+    Ring<KF, QL, PAGED>::kWgsPerCu * RowSplit<QL>::kGroups))) void mla_split_kernel(SplitParams p) {
   using RG = Ring<KF, QL, PAGED>;
+  constexpr int kThreads = Geom<KF>::kThreads * RowSplit<QL>::kGroups;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kLdsBytes];
   __shared__ float xchg[RG::kXchg / 4];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[QL > 1 ? RG::kPBuf : 16];
@@ -1301,10 +1333,10 @@ __global__ __launch_bounds__(Geom<KF>::kThreads) __attribute__((amdgpu_waves_per
 
   // Sequences overlapping [lo, hi): b in [#{j>=1: indptr[j] <= lo}, #{j<bs: indptr[j] < hi}).
   if (tid < 2) counts[tid] = 0;
-  if (KF == DT_MXFP4) e8m0_lut[tid] = e8m0_f32(tid);  // one code per thread (256 threads)
+  if (KF == DT_MXFP4 && (kThreads == 256 || tid < 256)) e8m0_lut[tid] = e8m0_f32(tid);  // one code per thread
   __syncthreads();
   int c_first = 0, c_end = 0;
-  for (int j = tid; j <= p.batch; j += G::kThreads) {
+  for (int j = tid; j <= p.batch; j += kThreads) {
     const int64_t v = p.kv_indptr[j];
     c_first += (j >= 1 && v <= lo);
     c_end += (j < p.batch && v < hi);
@@ -1572,7 +1604,7 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 template <int QF, int KF, bool CAP, bool PAGED>
 void launch_split_v(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
-  const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads);
+  const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads * (pl->ql == 4 ? RowSplit<4>::kGroups : 1));
   if (pl->ql == 1)
     hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED>), grid, block, 0, st, sp);
   else if (pl->ql == 2)
