@@ -43,8 +43,8 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "eb2c1bd7f09b89fc621d0ddf05923e835f567351541d794967ec27b781356dd9",
-    "fetch_kib": 152176.8,
+    "source_sha256": "70fd1fa0c32cea2da825509162def4c071c513a7015d52511390b552fd4a62fd",
+    "fetch_kib": 152175.2,
     "write_kib": 8224.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,

@@ -335,10 +335,22 @@ def test_run_on_a_side_stream():
     _compare(_bf16_out_to_f64(out), ref, "side stream")
 
 
-def test_split_then_merge_equals_run():
-    """mla_decode_split followed by mla_decode_merge on one stream gives the same
-    bits as mla_decode_run (the two stages as separate calls)."""
-    w = synth.make_batch([900, 64, 3000, 1, 2500], "bf16", "fp8", seed=1001, name="split+merge")
+def _widened_batch(q_len, seed):
+    """Several query rows, a soft-cap and paged KV at once."""
+    w = synth.make_batch([900, 64, 3000, 1, 2500], "bf16", "fp8", seed=seed, name="widened",
+                         q_lens=[q_len, 1, q_len, 0, q_len])
+    w.logit_cap = 3.0
+    return synth.page_workload(w, seed=seed + 1, spare_rows=300)
+
+
+@pytest.mark.parametrize("widened", [False, True])
+def test_split_then_merge_equals_run(widened):
+    """mla_decode_split (or _split_paged) followed by mla_decode_merge on one
+    stream gives the same bits as mla_decode_run (or _run_paged)."""
+    if widened:
+        w = _widened_batch(4, 1011)
+    else:
+        w = synth.make_batch([900, 64, 3000, 1, 2500], "bf16", "fp8", seed=1001, name="split+merge")
     b = dev.upload(w)
     plan = dev.plan_for(b, rows_per_split=256)
     ws = dev.workspace_for(plan)
@@ -351,12 +363,17 @@ def test_split_then_merge_equals_run():
     assert torch.equal(a_out.view(torch.int16), b_out.view(torch.int16))
 
 
-def test_graph_replays_match_eager():
-    """mla_decode_run captured in a HIP graph (no memset nodes: the library
-    records none) and replayed several times, with eager work and a
-    synchronisation between replays; every replay must equal the eager result
-    bit for bit, and the oracle within tolerance."""
-    w = synth.make_batch([700, 1500, 33, 4096], "bf16", "fp8", seed=909, name="graph")
+@pytest.mark.parametrize("widened", [False, True])
+def test_graph_replays_match_eager(widened):
+    """mla_decode_run (or _run_paged with several query rows and a soft-cap)
+    captured in a HIP graph (no memset nodes: the library records none) and
+    replayed several times, with eager work and a synchronisation between
+    replays; every replay must equal the eager result bit for bit, and the
+    oracle within tolerance."""
+    if widened:
+        w = _widened_batch(2, 919)
+    else:
+        w = synth.make_batch([700, 1500, 33, 4096], "bf16", "fp8", seed=909, name="graph")
     b = dev.upload(w)
     plan = dev.plan_for(b, rows_per_split=256)
     ws = dev.workspace_for(plan)
