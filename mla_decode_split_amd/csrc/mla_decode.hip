@@ -19,8 +19,9 @@
 // 2g + (piece starts before the range ? 0 : 1), and stage 2 merges those.  This
 // balances rows, not sequences, so ragged batches keep every CU equally busy.
 //
-// Stage-1 workgroup: four wave64s (two workgroups per CU for bf16 and fp8 KV,
-// three for MXFP4; one wave of each on every SIMD) stream the 32-row KV tiles
+// Stage-1 workgroup (one query row per sequence): four wave64s (two workgroups
+// per CU for bf16 and fp8 KV, three for MXFP4; one wave of each on every SIMD)
+// stream the 32-row KV tiles
 // of a piece through a shared LDS ring filled by 16-byte global->LDS DMA.  Per
 // tile:
 //   QK : each wave computes the partial S^T (32 tokens x 16 heads) over its
@@ -400,17 +401,18 @@ __device__ inline int pv_row(int g, int i) { return (i < 4) ? 4 * g + i : 12 + 4
 constexpr int pv_row_base(int i) { return (i < 4) ? i : 12 + i; }  // pv_row(g, i) - 4g
 
 // Per-lane LDS byte offsets (within a tile) of the reads a lane (m, g) of
-// wave w makes.
-//   k[blk][par]: K operand of chunk c of token block blk is at k[blk][c & 1] + kstep * (c >> 1)
-//   x[blk][e]  : fp8 x fp8 path, 16-byte half e of the 32 key bytes of chunk c is at x[blk][e] + 128 c
-//   v[h]       : V rows; row pv_row(g, i) column group q starts at v[(i & 3) >> 1] + vrow(i) + vstep * q
-// and the same with this wave's share of the dims folded in:
-//   xw[blk][e] : x[blk][e] + 128 w (main chunk w of the fp8 x fp8 path)
-//   kr[blk]    : rope chunk w (waves 0, 1) of the fp8 x fp8 path
-//   kb[blk]    : bf16 / MXFP4 path, chunk w + 4k is at kb[blk] + kbstep * k
+// wave w makes:
+//   x[blk][e]  : fp8 keys, 16-byte half e of the 32 key bytes of chunk c of
+//                token block blk is at x[blk][e] + 128 c;
+//   v[h]       : V rows; row pv_row(g, i) column group q starts at
+//                v[(i & 3) >> 1] + vrow(i) + vstep * q (E2M1: q = w folded in);
+// and with this wave's share of the dims folded in:
+//   xw[blk][e] : fp8 keys, x[blk][e] + 128 w (main chunk w); E2M1 keys, the
+//                unit of the 32 codes of main chunk w (e = 0);
+//   kr[blk]    : rope chunk w (waves 0, 1) of the fp8 and E2M1 keys;
+//   kb[blk]    : bf16 keys, chunk w + 4k is at kb[blk] + 256 k.
 template <int KF>
 struct LaneOffs {
-  int k[2][2];
   int x[2][2];
   int v[2];
   int xw[2][2];
@@ -425,26 +427,18 @@ struct LaneOffs {
     for (int blk = 0; blk < 2; ++blk) {
       const int row = 16 * blk + m;
       const int f = Layout<KF>::swz(row);
-#pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        if constexpr (KF == DT_FP8) {
-          // dims 32c + 8g + [0, 8): unit 2c + (g >> 1), byte 8 (g & 1)
-          k[blk][par] = row * R + 16 * ((2 * par + (g >> 1)) ^ f) + 8 * (g & 1);
-          // dims 128c + 32g + [0, 32): units 8c + 2g + e
-          x[blk][par] = row * R + 16 * (4 * (g >> 1) + ((2 * (g & 1) + par) ^ f));
-        } else if constexpr (KF == DT_BF16) {
-          // dims 32c + 8g + [0, 8) as bf16: unit 4c + g
-          k[blk][par] = row * R + 16 * (g ^ f);
-          x[blk][par] = 0;
-        } else {
-          // dims 32c + 8g + [0, 8) as E2M1 pairs: unit c, byte 4g
-          k[blk][par] = row * R + 16 * (par ^ f) + 4 * g;
-          x[blk][par] = 0;
-        }
+      if constexpr (KF == DT_FP8) {
+        // fp8 keys, dims 128c + 32g + [0, 32): units 8c + 2g + e
+        const int base = row * R + 16 * (4 * (g >> 1));
+        x[blk][0] = base + 16 * ((2 * (g & 1)) ^ f);
+        x[blk][1] = base + 16 * ((2 * (g & 1) + 1) ^ f);
+      } else {
+        x[blk][0] = x[blk][1] = 0;
       }
     }
-    // the same formulas as k[][] with par = w & 1 (computed, not selected, so
-    // that the offsets stay in registers)
+    // fp8 rope: dims 32c + 8g + [0, 8) are unit 2c + (g >> 1), byte 8 (g & 1),
+    // for chunk c = 16 + w with par = w & 1 (computed, not selected, so that the
+    // offsets stay in registers)
     const int par = w & 1;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -872,11 +866,13 @@ struct RopeUnits<DT_MXFP4> {
   static constexpr int kFirst = 16, kCount = 2;
 };
 
-// LDS byte offsets (within a tile slot) of the probability exchange:
+// LDS byte offsets (within a tile slot) of the probability exchange of query
+// row 0 (later rows: p_ptr / max_ptr below):
 //   P slot of lane l (16 bytes): bf16 P of the eight tokens lane l feeds to the
 //     PV product, [block][wave] - row l >> 1, rope unit (l & 1);
 //   max slot of head h (16 bytes): the four waves' maxima of the head's scores;
-//   flag slot (16 bytes): per wave, whether a score passed the rescale slack.
+//   flag slots (16 bytes per four waves): per wave a word whose bit r says a
+//     score of query row r passed the rescale slack.
 template <int KF>
 __device__ inline int p_slot(int lane) {
   constexpr int R = Geom<KF>::kRow;
@@ -900,9 +896,9 @@ __device__ inline int flag_slot(int half) {
     return Geom<KF>::kRowBytes + 704 + 16 * half;
 }
 
-// P slot and max slot of query token t: token 0 in the tile's rope bytes, later
-// tokens in `pb`, the tile parity's kPTokBytes-sized records (t is a
-// compile-time index after unrolling, so the choice costs nothing).
+// P slot and max slot of query row t: row 0 in the tile's rope bytes, later
+// rows in `pb`, the tile parity's kPTokBytes-sized records (t is a
+// compile-time index after unrolling when there is one row group).
 template <int KF>
 __device__ inline uint8_t* p_ptr(uint8_t* st, uint8_t* pb, int t, int lane) {
   return t == 0 ? st + p_slot<KF>(lane) : pb + (t - 1) * kPTokBytes + 16 * lane;
