@@ -43,8 +43,8 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "70fd1fa0c32cea2da825509162def4c071c513a7015d52511390b552fd4a62fd",
-    "fetch_kib": 152175.2,
+    "source_sha256": "1a5d4a24b8beeaf233613b44f18338824ec6d3493cf3857cc314cf23d0366458",
+    "fetch_kib": 152177.8,
     "write_kib": 8224.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
