@@ -76,7 +76,8 @@ typedef struct mla_problem {
                          1: paged KV with page size 1 (the layout of the library decode call
                          on submission 753817's page, page_size 1 with kv_indices): CSR row j
                          is row kv_indices[j] of kv, and runs go through the _paged entry
-                         points.  bf16 and fp8 KV; MXFP4: MLA_ERR_UNSUPPORTED */
+                         points.  Any KV format (MXFP4 scale rows are indexed like
+                         their rows) */
 } mla_problem;
 
 /* Optional planner overrides (NULL = planner's choice for every field). */
@@ -160,8 +161,9 @@ mla_status mla_decode_run(const mla_plan* plan, const void* q, const float* q_sc
 /*
  * mla_decode_run for a plan made with kv_paged = 1.  The arguments are those of
  * mla_decode_run, with total_kv counting CSR rows, plus:
- *   kv_rows    rows of the kv buffer ([kv_rows][576] bf16 or fp8 codes); at most
- *              0xFFFFF000 bytes of rows (larger buffers: MLA_ERR_UNSUPPORTED).
+ *   kv_rows    rows of the kv buffer ([kv_rows][576] bf16 or fp8 codes, [kv_rows][288]
+ *              MXFP4 bytes with kv_scale [kv_rows][18]); at most 0xFFFFF000 bytes of
+ *              rows (larger buffers: MLA_ERR_UNSUPPORTED).
  *   kv_indices device int32 [total_kv], 4-byte aligned: CSR row j of the plan is
  *              row kv_indices[j] of kv.  An index outside [0, kv_rows) gives
  *              undefined output for its sequence, but every read stays inside the

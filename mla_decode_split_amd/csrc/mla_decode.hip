@@ -173,12 +173,16 @@ template <> struct RingCfg<DT_BF16, 4> { static constexpr int kStages = 3, kWgsP
 template <> struct RingCfg<DT_FP8, 4> { static constexpr int kStages = 6, kWgsPerCu = 1; };
 template <> struct RingCfg<DT_MXFP4, 4> { static constexpr int kStages = 8, kWgsPerCu = 1; };
 
-// Paged KV (bf16 and fp8 rows) adds the 1 KB index ring: fp8 keeps two
-// workgroups per CU with a three-slot ring, bf16 runs one with three slots.
+// Paged KV adds the 1 KB index ring: fp8 keeps two workgroups per CU with a
+// three-slot ring, bf16 runs one with three slots.  MXFP4 slots grow by 1 KB
+// (the gathered scale windows fill the scale chunk, so the rescale path's
+// maxima and flags move to an extra chunk); with one query row three
+// workgroups with three-slot rings (a few registers spilled) measured faster
+// than two with four (119 vs 125 µs on the ragged batch).
 template <int KF, int QL>
 struct PagedRingCfg {
-  static constexpr int kStages = KF == DT_FP8 ? (QL == 4 ? 6 : 3) : 3;
-  static constexpr int kWgsPerCu = KF == DT_FP8 ? (QL == 4 ? 1 : 2) : 1;
+  static constexpr int kStages = KF == DT_FP8 ? (QL == 4 ? 6 : 3) : KF == DT_MXFP4 ? (QL == 4 ? 6 : QL == 1 ? 3 : 4) : 3;
+  static constexpr int kWgsPerCu = KF == DT_BF16 ? 1 : KF == DT_MXFP4 && QL == 1 ? 3 : (QL == 4 ? 1 : 2);
 };
 
 template <int KF, int QL, bool PAGED>
@@ -186,16 +190,19 @@ struct Ring {
   using Cfg = std::conditional_t<PAGED, PagedRingCfg<KF, QL>, RingCfg<KF, QL>>;
   static constexpr int kStages = Cfg::kStages;
   static constexpr int kWgsPerCu = Cfg::kWgsPerCu;
-  static constexpr int kLdsBytes = kStages * Geom<KF>::kStageBytes;
+  // paged MXFP4: one more 1 KB chunk per slot for the rescale maxima and flags
+  static constexpr int kAuxBytes = PAGED && KF == DT_MXFP4 ? 1024 : 0;
+  static constexpr int kStageBytes = Geom<KF>::kStageBytes + kAuxBytes;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
   static constexpr int kXchg = QL * kXchgBytes;
   static constexpr int kPBuf = 2 * (QL - 1) * kPTokBytes;
   static constexpr int kLut = KF == DT_MXFP4 ? 1024 : 0;  // E8M0 code -> fp32 table
   static constexpr int kIdx = PAGED ? kIdxSlots * kTile * 4 : 0;
-  static constexpr int kTotal = kLdsBytes + kXchg + kPBuf + kLut + kIdx;
+  static constexpr int kDtab = PAGED && KF == DT_MXFP4 ? kStages * kTile : 0;  // scale window offsets
+  static constexpr int kTotal = kLdsBytes + kXchg + kPBuf + kLut + kIdx + kDtab;
   static_assert(kWgsPerCu * kTotal <= 160 * 1024, "resident workgroups per CU must fit the LDS");
   static_assert((kStages - 2) * Dma<KF, PAGED>::kMaxChunksPerWave <= 63, "vmcnt range");
   static_assert(kStages >= 2 && kStages - 3 <= 5, "tiles behind the one needed near the end: 0..5");
-  static_assert(!PAGED || KF != DT_MXFP4, "paged KV: bf16 and fp8 rows");
   static_assert(!PAGED || kIdxSlots >= kStages - 1 + kIdxLead, "index ring covers the tiles staged ahead");
 };
 
@@ -487,11 +494,31 @@ __device__ inline bf16x8 load_kw(const uint8_t* st, const LaneOffs<KF>& lo, int 
   return *(const bf16x8*)(st + lo.kb[blk] + 256 * k);
 }
 
+// Where a tile's E8M0 scale bytes sit in its LDS slot: row r's 18 bytes start
+// at at(r).  Contiguous KV: the DMA copies the 16-byte-aligned span holding the
+// tile's 576 bytes, so at(r) = kRowBytes + d + 18 r with d the span's lead.
+// Paged KV: each row's 18 bytes are gathered as the aligned 32-byte window
+// holding them, window r at kRowBytes + 32 r, and dt[r] (LDS) is the row's
+// offset in it.
+template <bool PAGED>
+struct ScaleRows;
+template <>
+struct ScaleRows<false> {
+  int sdelta;  // the span's lead d
+  __device__ inline int at(int r) const { return Geom<DT_MXFP4>::kRowBytes + sdelta + r * kScaleRow; }
+};
+template <>
+struct ScaleRows<true> {
+  const uint8_t* dt;
+  __device__ inline int at(int r) const { return Geom<DT_MXFP4>::kRowBytes + 32 * r + (int)dt[r]; }
+};
+
 // V^T operands (A of O^T = V^T P^T) for value columns 128q + 8m + j (j = 0..7):
 // a[j] element i = V[pv_row(g, i)][128q + 8m + j].  Rows at or past `valid`
 // are zero when MASK.
-template <int KF, bool MASK>
-__device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q, int m, int g, int sdelta, int valid,
+template <int KF, bool PAGED, bool MASK>
+__device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q, int m, int g, const ScaleRows<PAGED>& sc,
+                               int valid,
                                bf16x8 a[8]) {
   constexpr int R = Geom<KF>::kRow;
   uint32_t r[8][4];  // r[j][p] = bf16 pair (token 2p, token 2p+1) of column j
@@ -527,7 +554,7 @@ __device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q,
         x[i] = *(const u32x4*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 256 * q);
       } else {
         const uint32_t w = *(const uint32_t*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 64 * q);
-        const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + pv_row(g, i) * kScaleRow + 4 * q + (m >> 2)];
+        const uint32_t e = st[sc.at(pv_row(g, i)) + 4 * q + (m >> 2)];
         x[i] = __builtin_bit_cast(u32x4, fp4x8_bf16(w, lo.e8m0[e]));
       }
       if (MASK && pv_row(g, i) >= valid) x[i] = u32x4{0u, 0u, 0u, 0u};
@@ -758,9 +785,9 @@ struct QOperand {
 // lane & 15 of query token t (before any scaling).  The K operand is read once
 // per block and multiplied with every token's query; two independent chains
 // (the blocks) keep the matrix pipe busy.
-template <int QF, int KF, int QL>
+template <int QF, int KF, int QL, bool PAGED>
 __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF> (&qo)[QL], const LaneOffs<KF>& lo, int w,
-                               int m, int sdelta, f32x4 (&s)[QL][2]) {
+                               int m, const ScaleRows<PAGED>& sc, f32x4 (&s)[QL][2]) {
   using QO = QOperand<QF, KF>;
 #pragma unroll
   for (int t = 0; t < QL; ++t) {
@@ -802,7 +829,7 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF> (&qo)[Q
       // 4-bit data); the query operand holds the dims they pair with
       const u32x4 k4 = *(const u32x4*)(st + lo.xw[blk][0]);
       const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k4, u32x4{0u, 0u, 0u, 0u}, 0, 1, 2, 3, 4, 5, 6, 7));
-      const int e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + 4 * w + (threadIdx.x & 63) / 16];
+      const int e = st[sc.at(16 * blk + m) + 4 * w + (threadIdx.x & 63) / 16];
 #pragma unroll
       for (int t = 0; t < QL; ++t) {
         // formats: A = 4 (E2M1), B = 0 (fp8 E4M3); B scale exponent 127 = 2^0
@@ -816,7 +843,7 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF> (&qo)[Q
       for (int blk = 0; blk < 2; ++blk) {
         // rope dims 512 + 32w + 8g + [0, 8), widened to bf16 with their block scale
         const uint32_t word = *(const uint32_t*)(st + lo.kr[blk]);
-        const uint32_t e = st[Geom<KF>::kRowBytes + sdelta + (16 * blk + m) * kScaleRow + 16 + w];
+        const uint32_t e = st[sc.at(16 * blk + m) + 16 + w];
         const bf16x8 kb = fp4x8_bf16(word, lo.e8m0[e]);
 #pragma unroll
         for (int t = 0; t < QL; ++t)
@@ -879,21 +906,24 @@ __device__ inline int p_slot(int lane) {
   const int row = lane >> 1;
   return row * R + 16 * ((RopeUnits<KF>::kFirst + (lane & 1)) ^ Layout<KF>::swz(row));
 }
-template <int KF>
+// E2M1 rows have two rope units: the maxima and flags go to the unused tail of
+// the tile's scale chunk, or (paged KV, where gathered scale windows fill that
+// chunk) to the same offsets of the slot's extra chunk after it.
+template <int KF, bool PAGED>
 __device__ inline int max_slot(int h) {
   constexpr int R = Geom<KF>::kRow;
   if constexpr (RopeUnits<KF>::kCount >= 4)
     return h * R + 16 * ((RopeUnits<KF>::kFirst + 2) ^ Layout<KF>::swz(h));
-  else  // E2M1 rows have two rope units: the unused tail of the tile's scale chunk
-    return Geom<KF>::kRowBytes + 768 + 16 * h;
+  else
+    return Geom<KF>::kRowBytes + (PAGED ? 1024 : 0) + 768 + 16 * h;
 }
 // flag words of waves 4 * half .. 4 * half + 3 (half 1 only with two row groups)
-template <int KF>
+template <int KF, bool PAGED>
 __device__ inline int flag_slot(int half) {
   if constexpr (RopeUnits<KF>::kCount >= 4)
     return half * Geom<KF>::kRow + 16 * ((RopeUnits<KF>::kFirst + 3) ^ Layout<KF>::swz(half));
   else
-    return Geom<KF>::kRowBytes + 704 + 16 * half;
+    return Geom<KF>::kRowBytes + (PAGED ? 1024 : 0) + 704 + 16 * half;
 }
 
 // P slot and max slot of query row t: row 0 in the tile's rope bytes, later
@@ -903,9 +933,9 @@ template <int KF>
 __device__ inline uint8_t* p_ptr(uint8_t* st, uint8_t* pb, int t, int lane) {
   return t == 0 ? st + p_slot<KF>(lane) : pb + (t - 1) * kPTokBytes + 16 * lane;
 }
-template <int KF>
+template <int KF, bool PAGED>
 __device__ inline uint8_t* max_ptr(uint8_t* st, uint8_t* pb, int t, int h) {
-  return t == 0 ? st + max_slot<KF>(h) : pb + (t - 1) * kPTokBytes + 64 * 16 + 16 * h;
+  return t == 0 ? st + max_slot<KF, PAGED>(h) : pb + (t - 1) * kPTokBytes + 64 * 16 + 16 * h;
 }
 
 // A tile goes through two steps, one ring barrier apart, so that every tile
@@ -948,15 +978,15 @@ struct TileScores {
 
 // tb: the first query row of this wave's group; w8: the wave in the workgroup
 // (w = w8 & 3 its share of dims and value columns).
-template <int QF, int KF, int QW, int NG, bool CAP, bool MASK>
+template <int QF, int KF, int QW, int NG, bool CAP, bool PAGED, bool MASK>
 __device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const QOperand<QF, KF> (&qo)[QW],
                                   const LaneOffs<KF>& lo, const WaveState (&ws)[QW], int w, int w8, int tb, int m, int g,
-                                  int sdelta, int valid, const float (&c)[QW], const SoftCap<QW, CAP>& cap,
+                                  const ScaleRows<PAGED>& sc, int valid, const float (&c)[QW], const SoftCap<QW, CAP>& cap,
                                   TileScores (&ts)[QW]) {
   const int lane = threadIdx.x & 63;
   {
     f32x4 part[QW][2];
-    qk_tile<QF, KF, QW>(st, qo, lo, w, m, sdelta, part);
+    qk_tile<QF, KF, QW, PAGED>(st, qo, lo, w, m, sc, part);
 #pragma unroll
     for (int t = 0; t < QW; ++t)
 #pragma unroll
@@ -991,23 +1021,24 @@ __device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const Q
   }
   if (lane == 0) {
     if constexpr (NG == 1)
-      ((int*)(st + flag_slot<KF>(0)))[w] = flags;
+      ((int*)(st + flag_slot<KF, PAGED>(0)))[w] = flags;
     else
-      ((int*)(st + flag_slot<KF>(w8 >> 2)))[w8 & 3] = flags;
+      ((int*)(st + flag_slot<KF, PAGED>(w8 >> 2)))[w8 & 3] = flags;
   }
 }
 
-template <int QF, int KF, int QW, int NG, bool MASK>
+template <int QF, int KF, int QW, int NG, bool PAGED, bool MASK>
 __device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>& lo, WaveState (&ws)[QW], int w, int tb,
-                                   int m, int g, int sdelta, int valid, const float (&c)[QW], TileScores (&ts)[QW]) {
+                                   int m, int g, const ScaleRows<PAGED>& sc, int valid, const float (&c)[QW],
+                                   TileScores (&ts)[QW]) {
   const int lane = threadIdx.x & 63;
   bf16x8 va[8];
-  load_vt<KF, MASK>(st, lo, w, m, g, sdelta, valid, va);
+  load_vt<KF, PAGED, MASK>(st, lo, w, m, g, sc, valid, va);
   // bit r: some wave flagged query row r (the same value in every wave)
-  const u32x4 fl = *(const u32x4*)(st + flag_slot<KF>(0));
+  const u32x4 fl = *(const u32x4*)(st + flag_slot<KF, PAGED>(0));
   uint32_t any = fl[0] | fl[1] | fl[2] | fl[3];
   if constexpr (NG == 2) {
-    const u32x4 f1 = *(const u32x4*)(st + flag_slot<KF>(1));
+    const u32x4 f1 = *(const u32x4*)(st + flag_slot<KF, PAGED>(1));
     any |= f1[0] | f1[1] | f1[2] | f1[3];
   }
   if (any != 0u) {
@@ -1018,13 +1049,13 @@ __device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>&
       float mx = fmaxf(ts[t].sv[0], ts[t].sv[1]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      if (g == 0) *(float*)(max_ptr<KF>(st, pb, tb + t, m) + 4 * w) = mx * c[t];
+      if (g == 0) *(float*)(max_ptr<KF, PAGED>(st, pb, tb + t, m) + 4 * w) = mx * c[t];
     }
     lds_barrier();
 #pragma unroll
     for (int t = 0; t < QW; ++t) {
       if (!((any >> (tb + t)) & 1u)) continue;
-      const f32x4 mw = *(const f32x4*)max_ptr<KF>(st, pb, tb + t, m);
+      const f32x4 mw = *(const f32x4*)max_ptr<KF, PAGED>(st, pb, tb + t, m);
       const float tmax = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
       const float m_new = fmaxf(ws[t].m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(ws[t].m_run - m_new);
@@ -1068,6 +1099,7 @@ __device__ inline void set_priority(int prio) {
 // last row and their results are dropped).
 template <int QF, int KF, int QL, bool CAP, bool PAGED>
 __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf, int32_t* idxring,
+                            uint8_t* dtab,
                             const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow0, int nq, int64_t r0,
                             int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
   using G = Geom<KF>;
@@ -1096,8 +1128,11 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   int64_t sbase = 0;
   i32x4 rs = rk;
   if constexpr (KF == DT_MXFP4) {
-    sbase = (r0 * kScaleRow) & ~(int64_t)15;
-    const uint64_t sbytes = (((uint64_t)p.total_kv * kScaleRow + 15) & ~15ull) - (uint64_t)sbase;
+    // E8M0 rows are read in 16-byte units: the allocation is readable up to the
+    // next multiple of 16 bytes past its rows (reads past it return zero)
+    const uint64_t rows = PAGED ? (uint64_t)p.kv_rows : (uint64_t)p.total_kv;
+    sbase = PAGED ? 0 : (r0 * kScaleRow) & ~(int64_t)15;
+    const uint64_t sbytes = ((rows * kScaleRow + 15) & ~15ull) - (uint64_t)sbase;
     rs = make_rsrc(p.kv_scale + sbase, (uint32_t)std::min<uint64_t>(sbytes, 0xFFFFF000ull));
   }
 
@@ -1115,16 +1150,22 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   }
   auto issue_tile = [&](int t) {
     if (wd >= DM::kWaves) return;
-    const uint8_t* stage = ring + (t % NS) * G::kStageBytes;
+    const uint8_t* stage = ring + (t % NS) * Ring<KF, QL, PAGED>::kStageBytes;
     const int32_t* ix = idxring + (t % kIdxSlots) * kTile;
 #pragma unroll
     for (int k = 0; k < DM::kMaxChunksPerWave; ++k) {
       const int c = wd + DM::kWaves * k;
       if (c >= G::kChunks) break;
-      if (PAGED) {
+      if (PAGED && c < G::kRowChunks) {
         // physical row of this lane's tile row (an index outside the buffer
         // wraps or lands past its end, where the read returns zero)
         dma16(rk, uniform(lds_addr(stage + c * 1024)), (uint32_t)ix[prow[k]] * (uint32_t)G::kRow + src[k]);
+      } else if (PAGED) {
+        // E8M0 bytes of tile row lane >> 1: the aligned 32-byte window holding
+        // its 18 (two 16-byte halves), and the row's offset in it
+        const uint32_t sb = (uint32_t)ix[lane >> 1] * (uint32_t)kScaleRow;
+        dma16(rs, uniform(lds_addr(stage + G::kRowBytes)), (sb & ~15u) + 16u * (uint32_t)(lane & 1));
+        if ((lane & 1) == 0) dtab[(t % NS) * kTile + (lane >> 1)] = (uint8_t)(sb & 15u);
       } else if (c < G::kRowChunks) {
         dma16(rk, uniform(lds_addr(stage + c * 1024)), (uint32_t)(t * G::kRowBytes) + src[k]);
       } else {
@@ -1202,8 +1243,11 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   auto refill = [&](int i) {
     if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
   };
-  auto sdelta_of = [&](int i) {
-    return (KF == DT_MXFP4) ? (int)(((r0 + (int64_t)i * kTile) * kScaleRow) & 15) : 0;
+  auto scales_of = [&](int i) -> ScaleRows<PAGED> {
+    if constexpr (PAGED)
+      return ScaleRows<true>{dtab + (i % NS) * kTile};
+    else
+      return ScaleRows<false>{(KF == DT_MXFP4) ? (int)(((r0 + (int64_t)i * kTile) * kScaleRow) & 15) : 0};
   };
   // full tiles in the loop (one code path, so the accumulators stay in place);
   // a partial last tile after it
@@ -1234,7 +1278,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
     cap.k[t] = live ? 2.f * cs[t] / p.logit_cap : 0.f;
   }
   const int last_valid = n - (ntiles - 1) * kTile;
-  auto stage = [&](int i) { return ring + (i % NS) * G::kStageBytes; };
+  auto stage = [&](int i) { return ring + (i % NS) * Ring<KF, QL, PAGED>::kStageBytes; };
   // probability records of tokens >= 1: one set per tile parity
   auto pbuf_of = [&](int i) { return pbuf + (i & 1) * ((QL - 1) * kPTokBytes); };
   TileScores ts[QW];
@@ -1243,32 +1287,32 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   advance(0);
   idx_step(0);
   if (nfull > 0)
-    score_tile<QF, KF, QW, NG, CAP, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(0), kTile, cs, cap, ts);
+    score_tile<QF, KF, QW, NG, CAP, PAGED, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, w8, tb, m, g, scales_of(0), kTile, cs, cap, ts);
   else
-    score_tile<QF, KF, QW, NG, CAP, true>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(0), last_valid, cs, cap,
+    score_tile<QF, KF, QW, NG, CAP, PAGED, true>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, w8, tb, m, g, scales_of(0), last_valid, cs, cap,
                                  ts);
   refill(0);
   for (int i = 1; i < nfull; ++i) {
     priority(i);
     advance(i);
     idx_step(i);
-    finish_tile<QF, KF, QW, NG, false>(stage(i - 1), pbuf_of(i - 1), lo, ws, w, tb, m, g, sdelta_of(i - 1), kTile, cs, ts);
-    score_tile<QF, KF, QW, NG, CAP, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(i), kTile, cs, cap, ts);
+    finish_tile<QF, KF, QW, NG, PAGED, false>(stage(i - 1), pbuf_of(i - 1), lo, ws, w, tb, m, g, scales_of(i - 1), kTile, cs, ts);
+    score_tile<QF, KF, QW, NG, CAP, PAGED, false>(stage(i), pbuf_of(i), xchg, qop, lo, ws, w, w8, tb, m, g, scales_of(i), kTile, cs, cap, ts);
     refill(i);
   }
   if (nfull > 0 && nfull < ntiles) {  // the partial last tile
     advance(nfull);
-    finish_tile<QF, KF, QW, NG, false>(stage(nfull - 1), pbuf_of(nfull - 1), lo, ws, w, tb, m, g, sdelta_of(nfull - 1), kTile,
+    finish_tile<QF, KF, QW, NG, PAGED, false>(stage(nfull - 1), pbuf_of(nfull - 1), lo, ws, w, tb, m, g, scales_of(nfull - 1), kTile,
                                    cs, ts);
-    score_tile<QF, KF, QW, NG, CAP, true>(stage(nfull), pbuf_of(nfull), xchg, qop, lo, ws, w, w8, tb, m, g, sdelta_of(nfull),
+    score_tile<QF, KF, QW, NG, CAP, PAGED, true>(stage(nfull), pbuf_of(nfull), xchg, qop, lo, ws, w, w8, tb, m, g, scales_of(nfull),
                                  last_valid, cs, cap, ts);
   }
   lds_barrier();  // the last tile's probabilities are in LDS
   if (nfull < ntiles)
-    finish_tile<QF, KF, QW, NG, true>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, tb, m, g, sdelta_of(ntiles - 1),
+    finish_tile<QF, KF, QW, NG, PAGED, true>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, tb, m, g, scales_of(ntiles - 1),
                                   last_valid, cs, ts);
   else
-    finish_tile<QF, KF, QW, NG, false>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, tb, m, g, sdelta_of(ntiles - 1),
+    finish_tile<QF, KF, QW, NG, PAGED, false>(stage(ntiles - 1), pbuf_of(ntiles - 1), lo, ws, w, tb, m, g, scales_of(ntiles - 1),
                                    kTile, cs, ts);
 
   if (PAGED && wd == 3) wait_vmcnt<0>();  // no index load outlives the piece
@@ -1319,6 +1363,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[QL > 1 ? RG::kPBuf : 16];
   __shared__ float e8m0_lut[KF == DT_MXFP4 ? 256 : 1];
   __shared__ __attribute__((aligned(16))) int32_t idxring[PAGED ? kIdxSlots * kTile : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t dtab[RG::kDtab ? RG::kDtab : 1];
   int* counts = (int*)xchg;  // the sequence search runs before any exchange
 
   const int tid = threadIdx.x;
@@ -1373,7 +1418,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
-    split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
+    split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
                             r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
     lds_barrier();  // the next piece refills the ring
   }
@@ -1577,7 +1622,7 @@ RingInfo ring_info_for(int kv_dtype, bool paged) {
   switch (kv_dtype) {
     case DT_BF16: return paged ? ring_info<DT_BF16, QL, true>() : ring_info<DT_BF16, QL, false>();
     case DT_FP8: return paged ? ring_info<DT_FP8, QL, true>() : ring_info<DT_FP8, QL, false>();
-    default: return ring_info<DT_MXFP4, QL, false>();  // paged MXFP4 is refused by the planner
+    default: return paged ? ring_info<DT_MXFP4, QL, true>() : ring_info<DT_MXFP4, QL, false>();
   }
 }
 
@@ -1619,13 +1664,10 @@ void launch_split_p(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
 
 template <int QF, int KF>
 hipError_t launch_split(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
-  if constexpr (KF != DT_MXFP4) {
-    if (pl->prob.kv_paged) {
-      launch_split_p<QF, KF, true>(pl, sp, st);
-      return hipGetLastError();
-    }
-  }
-  launch_split_p<QF, KF, false>(pl, sp, st);
+  if (pl->prob.kv_paged)
+    launch_split_p<QF, KF, true>(pl, sp, st);
+  else
+    launch_split_p<QF, KF, false>(pl, sp, st);
   return hipGetLastError();
 }
 
@@ -1659,7 +1701,6 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   if (pr->max_q_len < 0 || pr->max_q_len > 4) return MLA_ERR_UNSUPPORTED;
   if (!(pr->logit_cap >= 0.f) || !(pr->logit_cap < INFINITY)) return MLA_ERR_INVALID_ARG;
   if (pr->kv_paged != 0 && pr->kv_paged != 1) return MLA_ERR_INVALID_ARG;
-  if (pr->kv_paged && pr->kv_dtype == DT_MXFP4) return MLA_ERR_UNSUPPORTED;
   const int ql = pr->max_q_len <= 1 ? 1 : pr->max_q_len == 2 ? 2 : 4;
   if (ql == 1 && pr->total_q != pr->batch_size) return MLA_ERR_UNSUPPORTED;  // one query token per sequence
   if (ql > 1 && (pr->total_q < 1 || (int64_t)pr->total_q > (int64_t)pr->batch_size * pr->max_q_len))
@@ -1816,7 +1857,7 @@ mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, cons
   const mla_problem& pr = pl->prob;
   if ((kv_indices != nullptr) != (pr.kv_paged != 0)) return MLA_ERR_INVALID_ARG;
   if (kv_indices) {
-    const int64_t row_bytes = pr.kv_dtype == DT_BF16 ? 2 * kQK : kQK;
+    const int64_t row_bytes = pr.kv_dtype == DT_BF16 ? 2 * kQK : pr.kv_dtype == DT_FP8 ? kQK : kQK / 2;
     if (((uintptr_t)kv_indices & 3u) || kv_rows < 1) return MLA_ERR_INVALID_ARG;
     if (kv_rows > (int64_t)0xFFFFF000 / row_bytes) return MLA_ERR_UNSUPPORTED;  // 32-bit row offsets
   }

@@ -260,15 +260,18 @@ def test_soft_cap_saturating_scores():
 
 # ------------------------------------------------------------- paged KV (page size 1)
 
-PAGED_COMBOS = [c for c in COMBOS if c[1] != "mxfp4"]
+PAGED_COMBOS = COMBOS
 
 
 def _paged_equals_contiguous(w, pw, rows_per_split=0, what=""):
     """The paged run reads the same CSR rows as the contiguous one, through the
-    indices: the outputs agree bit for bit."""
+    indices: with the same cut (the paged plan's, whose residency may differ)
+    the outputs agree bit for bit."""
     b, pb = dev.upload(w), dev.upload(pw)
-    o1 = dev.run(dev.plan_for(b, rows_per_split=rows_per_split), b)
-    o2 = dev.run(dev.plan_for(pb, rows_per_split=rows_per_split), pb)
+    paged_plan = dev.plan_for(pb, rows_per_split=rows_per_split)
+    rows = mla.mla_decode_plan_describe(paged_plan)["rows_per_split"]
+    o1 = dev.run(dev.plan_for(b, rows_per_split=rows), b)
+    o2 = dev.run(paged_plan, pb)
     torch.cuda.synchronize()
     same = bool(torch.equal(o1.view(torch.int16), o2.view(torch.int16)))
     _say(f"{what}: paged == contiguous bitwise: {same}")
@@ -283,7 +286,7 @@ def test_paged_edge_lengths(q_dtype, kv_dtype):
     _paged_equals_contiguous(w, pw, what=f"paged {q_dtype}/{kv_dtype}")
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("rows", [32, 96, 512])
 def test_paged_query_rows_cap_and_splits(kv_dtype, rows):
     w = synth.make_batch([700, 0, 33, 1000, 1, 257], "bf16", kv_dtype, seed=161, name="paged-mix",
@@ -298,6 +301,19 @@ def test_paged_plan_without_host_indptr():
     w = synth.make_batch([100, 7, 900, 64], "bf16", "fp8", seed=171, name="paged-no-host")
     pw = synth.page_workload(w, seed=172, spare_rows=64)
     _check_batch(pw, use_host_indptr=False, rows_per_split=128, what="paged, plan without host indptr")
+
+
+def test_paged_mxfp4_ragged_full_size_sampled():
+    # the ragged MXFP4 batch scattered over a buffer with 1/16 spare rows (every
+    # scale-row offset in its 16-byte unit occurs), sampled against the oracle,
+    # the whole output bitwise against the contiguous run
+    w = synth.make_workload("bs128_ragged_mxfp4")
+    pw = synth.page_workload(w, seed=191, spare_rows=w.total_kv // 16)
+    lengths = np.diff(w.kv_indptr)
+    order = np.argsort(lengths)
+    ids = sorted(set(order[[0, 1, len(order) // 2, -2, -1]].tolist()))
+    _check_batch(pw, seq_ids=ids, poison=False, what=f"ragged mxfp4 paged (sequences {ids})")
+    _paged_equals_contiguous(w, pw, what="ragged mxfp4 paged")
 
 
 def test_paged_full_size_sampled():
