@@ -43,8 +43,8 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "1a5d4a24b8beeaf233613b44f18338824ec6d3493cf3857cc314cf23d0366458",
-    "fetch_kib": 152177.8,
+    "source_sha256": "63876a5daec883de82bb1ea9684da5dc950a42d9c095290063ba7afe50a551fb",
+    "fetch_kib": 152179.2,
     "write_kib": 8224.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,

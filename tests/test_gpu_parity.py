@@ -170,6 +170,19 @@ def test_plan_without_host_indptr_matches():
     _check_batch(w, use_host_indptr=True, rows_per_split=2048, what="single split per sequence (no stage 2)")
 
 
+def test_many_short_sequences():
+    # 1000 sequences (more than the merge kernel's argument table holds, and
+    # several passes of the stage-1 sequence search), lengths 0..300 with a
+    # few empty, two query rows each
+    lengths = synth.uniform_lengths(77, synth.STREAM_LEN, 1000, 0, 300)
+    w = synth.make_batch(lengths, "bf16", "fp8", seed=777, name="many", q_lens=[2] * 1000)
+    (_, _), plan, out = _check_batch(w, what="1000 short sequences, two query rows")
+    assert mla.mla_decode_plan_describe(plan)["stage2"] == 1
+    o = out.float().cpu().numpy()
+    for b in np.flatnonzero(lengths == 0)[:5]:
+        assert np.all(o[2 * b:2 * b + 2] == 0.0)
+
+
 def test_long_single_sequence():
     w = synth.make_batch([20000], "bf16", "fp8", seed=505, name="long")
     _check_batch(w, what="one sequence of 20000 rows")
