@@ -1454,8 +1454,7 @@ constexpr int kMergeBatch = 8;
 constexpr int kMergeTable = 512;
 struct MergeTable {
   static constexpr bool kHas = true;
-  uint16_t g0[kMergeTable];
-  uint16_t g1[kMergeTable];
+  uint32_t g01[kMergeTable];  // g0 | g1 << 16: one scalar load per sequence
 };
 struct NoMergeTable {
   static constexpr bool kHas = false;
@@ -1478,8 +1477,12 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
   uint16_t* o = p.out + (qrow * kHeads + h) * kV + 4 * t;
   int32_t g0, g1;
   if constexpr (Tab::kHas) {
-    g0 = tab.g0[b];
-    g1 = tab.g1[b];
+    const uint32_t v = tab.g01[b];
+    // the output row is needed only by the final store: have its load complete
+    // together with the table read rather than after the merge
+    if constexpr (QL == 1) asm volatile("" ::"s"((int32_t)qrow), "s"(v));
+    g0 = (int32_t)(v & 0xffffu);
+    g1 = (int32_t)(v >> 16);
   } else {
     const int64_t s = std::max<int64_t>(p.kv_indptr[b], 0);
     const int64_t e = std::min<int64_t>(p.kv_indptr[b + 1], p.total_kv);
@@ -1513,13 +1516,16 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     float mx = m_run;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) mx = fmaxf(mx, lse[k]);
-    if (mx == -INFINITY) continue;  // only empty slices so far
-    const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - mx);
+    // only empty slices so far (mx = -inf): every weight and alpha is 0 and the
+    // sums stay 0, with no branch (a branch here lets the compiler hold the
+    // partial loads back until the maxima are known)
+    const float mref = mx == -INFINITY ? 0.f : mx;
+    const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - mref);
     wsum *= alpha;
     acc *= alpha;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const float wgt = (lse[k] == -INFINITY) ? 0.f : __expf(lse[k] - mx);
+      const float wgt = (lse[k] == -INFINITY) ? 0.f : __expf(lse[k] - mref);
       wsum += wgt;
       acc += wgt * v[k];
     }
@@ -1768,8 +1774,8 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
       const int64_t e = std::min<int64_t>(kv_indptr_host[b + 1], total);
       const int64_t g0 = std::min<int64_t>(s / R, G - 1);
       const int64_t g1 = e > s ? std::min<int64_t>((e - 1) / R, G - 1) : g0 - 1;
-      pl->table.g0[b] = (uint16_t)(g1 < g0 ? 1 : g0);  // empty: g0 = 1 > g1 = 0
-      pl->table.g1[b] = (uint16_t)(g1 < g0 ? 0 : g1);
+      // empty: g0 = 1 > g1 = 0
+      pl->table.g01[b] = g1 < g0 ? 1u : (uint32_t)g0 | ((uint32_t)g1 << 16);
     }
   }
   pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
