@@ -1438,8 +1438,8 @@ struct MergeParams {
   int32_t num_wgs;
 };
 
-// One workgroup of 128 threads per (sequence, query token, head); thread i owns
-// columns 4i..4i+3.  The log-sum-exps and partial outputs of up to kMergeBatch
+// One workgroup of two waves per (sequence, query token, pair of heads); wave w
+// takes head 2j + w and its lane i columns 8i..8i+7 (16-byte loads).  The log-sum-exps and partial outputs of up to kMergeBatch
 // slots are loaded together (none depends on another), then combined with a
 // running maximum, so a sequence of up to kMergeBatch pieces costs one round
 // trip to memory after the index loads.  Partial slot s holds QL query tokens:
@@ -1462,9 +1462,10 @@ struct NoMergeTable {
 
 template <typename Tab, int QL>
 __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) {
-  const int bt = blockIdx.x >> 4, h = blockIdx.x & 15;
+  // two heads per workgroup: wave w of head 2 (blockIdx & 7) + w, 8 columns per lane
+  const int bt = blockIdx.x >> 3, h = 2 * (blockIdx.x & 7) + (threadIdx.x >> 6);
   const int b = bt / QL, tq = bt % QL;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x & 63;
   int64_t qrow;
   if constexpr (QL == 1) {
     qrow = std::min(std::max(p.qo_indptr[b], 0), p.total_q - 1);
@@ -1474,7 +1475,7 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     // the same query rows stage 1 takes: at most QL, inside the q buffer
     if (tq >= (int64_t)q1 - q0 || q0 < 0 || qrow >= p.total_q) return;
   }
-  uint16_t* o = p.out + (qrow * kHeads + h) * kV + 4 * t;
+  uint16_t* o = p.out + (qrow * kHeads + h) * kV + 8 * t;
   int32_t g0, g1;
   if constexpr (Tab::kHas) {
     const uint32_t v = tab.g01[b];
@@ -1490,29 +1491,32 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     g1 = e > s ? (int32_t)std::min<int64_t>((e - 1) / p.rows_per_wg, p.num_wgs - 1) : g0 - 1;
   }
   if (g1 < g0) {  // no KV rows: the softmax is empty, the output is zero
-    *(uint2*)o = make_uint2(0u, 0u);
+    *(u32x4*)o = u32x4{0u, 0u, 0u, 0u};
     return;
   }
   if (g0 == g1) return;  // written by stage 1
   float m_run = -INFINITY, wsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
   for (int32_t base = g0; base <= g1; base += kMergeBatch) {
     // straight-line loads (slots past g1 re-read slot g1 and get weight 0), so
     // that they are all in flight before the first is used
     float lse[kMergeBatch];
-    uint2 u[kMergeBatch];
+    u32x4 u[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const int64_t slot = (int64_t)merge_slot(std::min(base + k, g1), g0) * QL + tq;
       lse[k] = p.part_lse[slot * kHeads + h];
-      u[k] = *(const uint2*)(p.part_o + (slot * kHeads + h) * kV + 4 * t);
+      u[k] = *(const u32x4*)(p.part_o + (slot * kHeads + h) * kV + 8 * t);
     }
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k)
       if (base + k > g1) lse[k] = -INFINITY;
-    f32x4 v[kMergeBatch];
+    f32x4 v[kMergeBatch], v2[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) v[k] = f32x4{bf_lo(u[k].x), bf_hi(u[k].x), bf_lo(u[k].y), bf_hi(u[k].y)};
+    for (int k = 0; k < kMergeBatch; ++k) {
+      v[k] = f32x4{bf_lo(u[k][0]), bf_hi(u[k][0]), bf_lo(u[k][1]), bf_hi(u[k][1])};
+      v2[k] = f32x4{bf_lo(u[k][2]), bf_hi(u[k][2]), bf_lo(u[k][3]), bf_hi(u[k][3])};
+    }
     float mx = m_run;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) mx = fmaxf(mx, lse[k]);
@@ -1523,16 +1527,19 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - mref);
     wsum *= alpha;
     acc *= alpha;
+    acc2 *= alpha;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const float wgt = (lse[k] == -INFINITY) ? 0.f : __expf(lse[k] - mref);
       wsum += wgt;
       acc += wgt * v[k];
+      acc2 += wgt * v2[k];
     }
     m_run = mx;
   }
   const float inv = 1.f / wsum;
-  *(uint2*)o = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  *(u32x4*)o = u32x4{pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv),
+                     pack_bf16x2(acc2.x * inv, acc2.y * inv), pack_bf16x2(acc2.z * inv, acc2.w * inv)};
 }
 
 // ---------------------------------------------------------------- decode check
@@ -1917,7 +1924,7 @@ mla_status launch_split_stage(const mla_plan* pl, const SplitParams& sp, hipStre
 
 mla_status launch_merge_stage(const mla_plan* pl, const MergeParams& mp, hipStream_t st) {
   if (!pl->stage2) return MLA_OK;
-  const dim3 grid(pl->prob.batch_size * pl->ql * kHeads), block(128);
+  const dim3 grid(pl->prob.batch_size * pl->ql * kHeads / 2), block(128);
   if (pl->has_table) {
     if (pl->ql == 1)
       hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 1>), grid, block, 0, st, mp, pl->table);
