@@ -502,15 +502,25 @@ __device__ inline bf16x8 load_kw(const uint8_t* st, const LaneOffs<KF>& lo, int 
 // offset in it.
 template <bool PAGED>
 struct ScaleRows;
+// at(rl, rc): tile offset of row rl + rc's scale bytes, rl per lane, rc a
+// compile-time constant.
 template <>
 struct ScaleRows<false> {
   int sdelta;  // the span's lead d
-  __device__ inline int at(int r) const { return Geom<DT_MXFP4>::kRowBytes + sdelta + r * kScaleRow; }
+  __device__ inline int at(int rl, int rc) const { return Geom<DT_MXFP4>::kRowBytes + sdelta + (rl + rc) * kScaleRow; }
 };
 template <>
 struct ScaleRows<true> {
   const uint8_t* dt;
-  __device__ inline int at(int r) const { return Geom<DT_MXFP4>::kRowBytes + 32 * r + (int)dt[r]; }
+  // The empty asm keeps rc's part out of the per-lane sum, so that it ends in
+  // the LDS read's immediate offset: otherwise the compiler keeps one register
+  // per row (32 (rl + rc) with the bits of rl and rc merged), which at three
+  // workgroups per CU spills.
+  __device__ inline int at(int rl, int rc) const {
+    int a = 32 * rl + (int)dt[rl + rc];
+    asm("" : "+v"(a));
+    return a + Geom<DT_MXFP4>::kRowBytes + 32 * rc;
+  }
 };
 
 // V^T operands (A of O^T = V^T P^T) for value columns 128q + 8m + j (j = 0..7):
@@ -554,7 +564,7 @@ __device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q,
         x[i] = *(const u32x4*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 256 * q);
       } else {
         const uint32_t w = *(const uint32_t*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 64 * q);
-        const uint32_t e = st[sc.at(pv_row(g, i)) + 4 * q + (m >> 2)];
+        const uint32_t e = st[sc.at(4 * g, pv_row_base(i)) + 4 * q + (m >> 2)];
         x[i] = __builtin_bit_cast(u32x4, fp4x8_bf16(w, lo.e8m0[e]));
       }
       if (MASK && pv_row(g, i) >= valid) x[i] = u32x4{0u, 0u, 0u, 0u};
@@ -829,7 +839,7 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF> (&qo)[Q
       // 4-bit data); the query operand holds the dims they pair with
       const u32x4 k4 = *(const u32x4*)(st + lo.xw[blk][0]);
       const i32x8 k = __builtin_bit_cast(i32x8, __builtin_shufflevector(k4, u32x4{0u, 0u, 0u, 0u}, 0, 1, 2, 3, 4, 5, 6, 7));
-      const int e = st[sc.at(16 * blk + m) + 4 * w + (threadIdx.x & 63) / 16];
+      const int e = st[sc.at(m, 16 * blk) + 4 * w + (threadIdx.x & 63) / 16];
 #pragma unroll
       for (int t = 0; t < QL; ++t) {
         // formats: A = 4 (E2M1), B = 0 (fp8 E4M3); B scale exponent 127 = 2^0
@@ -843,7 +853,7 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF> (&qo)[Q
       for (int blk = 0; blk < 2; ++blk) {
         // rope dims 512 + 32w + 8g + [0, 8), widened to bf16 with their block scale
         const uint32_t word = *(const uint32_t*)(st + lo.kr[blk]);
-        const uint32_t e = st[sc.at(16 * blk + m) + 16 + w];
+        const uint32_t e = st[sc.at(m, 16 * blk) + 16 + w];
         const bf16x8 kb = fp4x8_bf16(word, lo.e8m0[e]);
 #pragma unroll
         for (int t = 0; t < QL; ++t)
