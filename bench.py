@@ -43,7 +43,7 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "32e9f30965650149dae63189d8355879fa31f9c3b57a35fdcd40d6ba3115808b",
+    "source_sha256": "b96f776fab646280b91f5ba45bc12fe2a19d12f60b3243c6b9823cb90f95349a",
     "fetch_kib": 152179.3,
     "write_kib": 8224.0,
     "fetch_scale": 2.0,
