@@ -310,6 +310,20 @@ def test_paged_query_rows_cap_and_splits(kv_dtype, rows):
     _paged_equals_contiguous(w, pw, rows_per_split=rows, what=f"paged mix rows={rows} kv={kv_dtype}")
 
 
+@pytest.mark.parametrize("cap", [0.0, 2.5])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+def test_paged_two_query_rows(kv_dtype, cap):
+    # at most two query rows per sequence: the two-row paged kernels, with and
+    # without the soft-cap, against the oracle and bitwise against contiguous KV
+    w = synth.make_batch([700, 0, 33, 1000, 1, 257], "bf16", kv_dtype, seed=181, name="paged-q2",
+                         q_lens=[2, 1, 2, 0, 2, 1])
+    w.logit_cap = cap
+    pw = synth.page_workload(w, seed=182, spare_rows=100)
+    (_, _), plan, _ = _check_batch(pw, rows_per_split=96, what=f"paged, q rows <= 2, cap {cap}, kv={kv_dtype}")
+    assert mla.mla_decode_plan_describe(plan)["query_tokens"] == 2
+    _paged_equals_contiguous(w, pw, rows_per_split=96, what=f"paged q2 cap={cap} kv={kv_dtype}")
+
+
 def test_paged_plan_without_host_indptr():
     w = synth.make_batch([100, 7, 900, 64], "bf16", "fp8", seed=171, name="paged-no-host")
     pw = synth.page_workload(w, seed=172, spare_rows=64)
