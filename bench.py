@@ -229,8 +229,9 @@ class Timed:
 def main() -> int:
     args = _args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sequences shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(sequences would shard across GPUs with no exchange; each GPU runs this same path on its share)",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -40,7 +40,7 @@ extern "C" {
 typedef enum mla_status {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size, workspace too small, bad indptr */
-  MLA_ERR_UNSUPPORTED = 2, /* shape or dtype combination this build does not implement */
+  MLA_ERR_UNSUPPORTED = 2, /* shape or dtype combination the library does not implement */
   MLA_ERR_HIP = 3          /* a HIP call or kernel launch failed */
 } mla_status;
 
@@ -123,7 +123,7 @@ typedef struct mla_plan mla_plan;
  *                   batch_size and total_kv.
  *   plan_out        receives a library-owned plan; free with mla_decode_plan_destroy.
  *   workspace_bytes receives the size of the device workspace run needs.
- * Returns MLA_ERR_UNSUPPORTED for shapes/dtypes outside this build and
+ * Returns MLA_ERR_UNSUPPORTED for shapes/dtypes the library does not implement and
  * MLA_ERR_INVALID_ARG for bad arguments; *plan_out is NULL on failure.
  */
 mla_status mla_decode_plan(const mla_problem* problem, const mla_plan_options* options,
