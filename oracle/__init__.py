@@ -63,6 +63,9 @@ def _bind(lib):
     lib.oracle_mla_decode.restype = i32
     lib.oracle_mla_decode_paged.argtypes = [ctypes.POINTER(_Problem), vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32]
     lib.oracle_mla_decode_paged.restype = i32
+    lib.oracle_mla_decode_pages.argtypes = [ctypes.POINTER(_Problem), vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp,
+                                            vp, i32]
+    lib.oracle_mla_decode_pages.restype = i32
     return lib
 
 
@@ -113,7 +116,7 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 def mla_decode(q, kv, qo_indptr, kv_indptr, *, q_dtype="bf16", kv_dtype="bf16", q_scale=None, kv_scale=None,
                sm_scale=1.0 / 24.0, num_heads=16, qk_dim=576, v_dim=512, seq_ids=None, threads=1, lib=None,
-               logit_cap=0.0, kv_indices=None):
+               logit_cap=0.0, kv_indices=None, kv_page_indptr=None, page_size=1):
     """fp64 reference output and LSE.
 
     q: uint16 bf16 bits or uint8 fp8 codes, shape [total_q, num_heads, qk_dim].
@@ -122,6 +125,10 @@ def mla_decode(q, kv, qo_indptr, kv_indptr, *, q_dtype="bf16", kv_dtype="bf16", 
     kv_scale: fp32 scalar for fp8, uint8 [total_kv, qk_dim/32] for mxfp4.
     kv_indices: None, or int32 [kv_indptr[-1]]: KV row j of the CSR space is
         kv[kv_indices[j]] (paged KV, page size 1).
+    kv_page_indptr, page_size: paged KV with pages of page_size rows:
+        kv_indices lists pages, sequence b's from entry kv_page_indptr[b] on,
+        and its row i is kv[kv_indices[kv_page_indptr[b] + i // page_size] *
+        page_size + i % page_size].
     Returns (out [total_q, num_heads, v_dim] float64, lse [total_q, num_heads]);
     rows of sequences not in ``seq_ids`` are NaN."""
     lib = lib or load()
@@ -143,7 +150,18 @@ def mla_decode(q, kv, qo_indptr, kv_indptr, *, q_dtype="bf16", kv_dtype="bf16", 
     out = np.full((total_q, num_heads, v_dim), np.nan, dtype=np.float64)
     lse = np.full((total_q, num_heads), np.nan, dtype=np.float64)
     n_seq = prob.batch_size if ids is None else ids.shape[0]
-    if kv_indices is None:
+    if kv_page_indptr is not None:
+        ki = np.ascontiguousarray(kv_indices, dtype=np.int32)
+        kpp = np.ascontiguousarray(kv_page_indptr, dtype=np.int32)
+        P = int(page_size)
+        lens = np.diff(kvp.astype(np.int64))
+        need = kpp[:-1].astype(np.int64) + (lens + P - 1) // P
+        if P < 1 or kpp.shape[0] != kvp.shape[0] or (need.size and need.max() > ki.shape[0]) or \
+                (ki.size and (ki.min() < 0 or (int(ki.max()) + 1) * P > kv.shape[0])):
+            raise ValueError("the page lists must lie in kv_indices and name pages inside kv")
+        rc = lib.oracle_mla_decode_pages(ctypes.byref(prob), _p(q), _p(qs), _p(kv), _p(ks), _p(qo), _p(kvp), _p(ki),
+                                         _p(kpp), P, _p(ids), n_seq, _p(out), _p(lse), int(threads))
+    elif kv_indices is None:
         rc = lib.oracle_mla_decode(ctypes.byref(prob), _p(q), _p(qs), _p(kv), _p(ks), _p(qo), _p(kvp), _p(ids),
                                    n_seq, _p(out), _p(lse), int(threads))
     else:
@@ -162,4 +180,5 @@ def decode_workload(w, seq_ids=None, threads=1, lib=None):
     return mla_decode(w.q, w.kv, w.qo_indptr, w.kv_indptr, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
                       q_scale=w.q_scale, kv_scale=w.kv_scale, sm_scale=w.sm_scale, seq_ids=seq_ids,
                       threads=threads, lib=lib, logit_cap=getattr(w, "logit_cap", 0.0),
-                      kv_indices=getattr(w, "kv_indices", None))
+                      kv_indices=getattr(w, "kv_indices", None),
+                      kv_page_indptr=getattr(w, "kv_page_indptr", None), page_size=getattr(w, "page_size", 1))

@@ -27,10 +27,13 @@
  * Quantised inputs are used through their decoded values for both K and V:
  *   fp8 E4M3FN   value(code) * scale            (one fp32 scale per tensor)
  *   MXFP4        value_E2M1(nibble) * 2^(E8M0 - 127)   (one scale per 32 columns)
- * Paged KV (page size 1, the layout of the library decode call on submission
- * 753817's page, which passes kv_indices with page_size 1): the rows of
- * sequence b are KV[kv_indices[j]] for j in [kv_indptr[b], kv_indptr[b+1]).
- * Without kv_indices they are KV[j].
+ * Paged KV (the kv_indices / page_size arguments of the library decode call on
+ * submission 753817's page, which passes page_size 1): with page size 1 the
+ * rows of sequence b are KV[kv_indices[j]] for j in [kv_indptr[b],
+ * kv_indptr[b+1]).  With page size P > 1, kv_indices lists pages: row i of
+ * sequence b (i counted from 0) is row i mod P of page
+ * kv_indices[kv_page_indptr[b] + i div P], that is KV[page * P + i mod P].
+ * Without kv_indices the rows are KV[j].
  *
  * The fp8 a8w8 reference on the template page multiplies the two per-tensor
  * scales into the fp8 product (torch._scaled_mm with scale_a, scale_b), which
@@ -181,8 +184,8 @@ typedef struct {
   const oracle_problem* p;
   const void *q, *kv, *kv_scale;
   const float* q_scale;
-  const int32_t *qo_indptr, *kv_indptr, *kv_indices, *seq_ids;
-  int n_seq;
+  const int32_t *qo_indptr, *kv_indptr, *kv_indices, *kv_page_indptr, *seq_ids;
+  int n_seq, page_size;
   double *out, *lse;
   int next; /* shared work counter, guarded by mu */
   pthread_mutex_t mu;
@@ -217,7 +220,11 @@ static void* worker(void* arg) {
       }
     }
     for (int64_t j = 0; j < n; ++j) {
-      const int64_t row = sh->kv_indices ? (int64_t)sh->kv_indices[j0 + j] : j0 + j;
+      int64_t row = j0 + j;
+      if (sh->kv_page_indptr)
+        row = (int64_t)sh->kv_indices[sh->kv_page_indptr[b] + j / sh->page_size] * sh->page_size + j % sh->page_size;
+      else if (sh->kv_indices)
+        row = sh->kv_indices[j0 + j];
       decode_kv_row(p, sh->kv, sh->kv_scale, row, kvrows + j * D);
     }
     for (int64_t t = sh->qo_indptr[b]; t < sh->qo_indptr[b + 1]; ++t)
@@ -249,13 +256,30 @@ int oracle_mla_decode(const oracle_problem* p, const void* q, const float* q_sca
                                  nthreads);
 }
 
+int oracle_mla_decode_pages(const oracle_problem* p, const void* q, const float* q_scale, const void* kv,
+                            const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* kv_page_indptr, int page_size,
+                            const int32_t* seq_ids, int n_seq, double* out, double* lse, int nthreads);
+
 /* The same with KV row j of the CSR space read from KV[kv_indices[j]] (NULL:
  * KV[j]); the caller guarantees every index is a row of kv. */
 int oracle_mla_decode_paged(const oracle_problem* p, const void* q, const float* q_scale, const void* kv,
                             const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr,
                             const int32_t* kv_indices, const int32_t* seq_ids, int n_seq, double* out, double* lse,
                             int nthreads) {
+  return oracle_mla_decode_pages(p, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, kv_indices, NULL, 1, seq_ids,
+                                 n_seq, out, lse, nthreads);
+}
+
+/* The same with pages of page_size rows: kv_page_indptr[b] is the first entry
+ * of sequence b's page list in kv_indices (NULL: one index per CSR row, as
+ * above); the caller guarantees every page it names lies inside kv. */
+int oracle_mla_decode_pages(const oracle_problem* p, const void* q, const float* q_scale, const void* kv,
+                            const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* kv_page_indptr, int page_size,
+                            const int32_t* seq_ids, int n_seq, double* out, double* lse, int nthreads) {
   if (!p || !q || !kv || !qo_indptr || !kv_indptr || !out || !lse) return -1;
+  if (kv_page_indptr && (!kv_indices || page_size < 1)) return -1;
   if (p->num_heads <= 0 || p->qk_dim <= 0 || p->v_dim <= 0 || p->v_dim > p->qk_dim) return -1;
   if (!(p->logit_cap >= 0.0)) return -1;
   if (p->kv_dtype == ORACLE_MXFP4 && p->qk_dim % 32) return -1;
@@ -272,6 +296,8 @@ int oracle_mla_decode_paged(const oracle_problem* p, const void* q, const float*
   sh.qo_indptr = qo_indptr;
   sh.kv_indptr = kv_indptr;
   sh.kv_indices = kv_indices;
+  sh.kv_page_indptr = kv_page_indptr;
+  sh.page_size = page_size;
   sh.seq_ids = seq_ids;
   sh.n_seq = n_seq;
   sh.out = out;

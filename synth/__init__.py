@@ -179,6 +179,8 @@ class Workload:
     meta: dict = field(default_factory=dict)
     logit_cap: float = 0.0             # > 0: scores soft-capped as cap * tanh(s / cap)
     kv_indices: np.ndarray | None = None  # paged KV (page size 1): CSR row j is kv[kv_indices[j]]
+    kv_page_indptr: np.ndarray | None = None  # pages of page_size rows: sequence b's page list
+    page_size: int = 1                         # starts at kv_indices[kv_page_indptr[b]]
 
     @property
     def batch_size(self) -> int:
@@ -191,6 +193,8 @@ class Workload:
     @property
     def total_kv(self) -> int:
         """Rows of the CSR space (of the KV buffer when not paged)."""
+        if self.kv_page_indptr is not None:
+            return int(self.kv_indptr[-1])
         return int(self.kv.shape[0]) if self.kv_indices is None else int(self.kv_indices.shape[0])
 
     @property
@@ -252,31 +256,52 @@ def make_batch(lengths, q_dtype: str, kv_dtype: str, seed: int, name: str = "cus
                     meta={"seed": seed, "lengths": lengths, "q_lens": np.diff(qo_indptr)})
 
 
-def page_workload(w: Workload, seed: int, spare_rows: int = 0, threads: int | None = None) -> Workload:
+def page_workload(w: Workload, seed: int, spare_rows: int = 0, threads: int | None = None,
+                  page_size: int = 1) -> Workload:
     """The same batch with its KV rows scattered over a larger buffer (paged
-    KV, page size 1): a seeded random injective map sends CSR row j to
-    physical row kv_indices[j] of a buffer of total_kv + spare_rows rows; the
-    rows no index names hold fresh draws of the same format, so a wrong index
-    reads different data.  Only MXFP4 scale rows move with their rows."""
+    KV).  Page size 1: a seeded random injective map sends CSR row j to
+    physical row kv_indices[j] of a buffer of total_kv + spare_rows rows.
+    Page size P > 1: each sequence's rows fill ceil(len / P) pages, drawn by a
+    seeded random injective map from the buffer's pages (enough for the rows
+    plus spare_rows); kv_indices holds the page lists back to back and
+    kv_page_indptr[b] is where sequence b's begins.  Rows no sequence uses hold
+    fresh draws of the same format, so a wrong index reads different data.
+    Only MXFP4 scale rows move with their rows."""
     n = w.total_kv
-    rows = n + spare_rows
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0x9A6E]))
-    kv_indices = rng.permutation(rows)[:n].astype(np.int32)
+    kv_page_indptr = None
+    if page_size == 1:
+        rows = n + spare_rows
+        kv_indices = rng.permutation(rows)[:n].astype(np.int32)
+        dest = kv_indices.astype(np.int64)
+    else:
+        P = int(page_size)
+        lens = np.diff(np.asarray(w.kv_indptr, dtype=np.int64))
+        npages = (lens + P - 1) // P
+        kv_page_indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+        total_pages = int(kv_page_indptr[-1])
+        pages = total_pages + (spare_rows + P - 1) // P
+        rows = pages * P
+        kv_indices = rng.permutation(pages)[:total_pages].astype(np.int32)
+        # destination of each CSR row: its page's first row plus its place in the page
+        seq = np.repeat(np.arange(lens.shape[0]), lens)
+        within = np.arange(n, dtype=np.int64) - np.asarray(w.kv_indptr, dtype=np.int64)[seq]
+        dest = kv_indices[kv_page_indptr[seq] + within // P].astype(np.int64) * P + within % P
     filler = make_batch([rows], "bf16", w.kv_dtype, seed=seed + 1000003, threads=threads)
     kv = filler.kv.copy()
-    kv[kv_indices] = w.kv
+    kv[dest] = w.kv
     kv_scale = w.kv_scale
     if w.kv_dtype == "mxfp4":
         kv_scale = filler.kv_scale.copy()
-        kv_scale[kv_indices] = w.kv_scale
+        kv_scale[dest] = w.kv_scale
     elif w.kv_dtype == "fp8":
         # the filler was quantised with its own scale: re-encode nothing, the
         # per-tensor scale of the batch applies to every row of the buffer
         kv_scale = w.kv_scale
     out = Workload(name=w.name + "_paged", q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, q=w.q, q_scale=w.q_scale, kv=kv,
                    kv_scale=kv_scale, qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr, sm_scale=w.sm_scale,
-                   meta=dict(w.meta, paged_seed=seed, spare_rows=spare_rows), logit_cap=w.logit_cap,
-                   kv_indices=kv_indices)
+                   meta=dict(w.meta, paged_seed=seed, spare_rows=spare_rows, page_size=page_size),
+                   logit_cap=w.logit_cap, kv_indices=kv_indices, kv_page_indptr=kv_page_indptr, page_size=page_size)
     return out
 
 

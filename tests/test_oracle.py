@@ -399,6 +399,55 @@ def test_paged_identity_and_repeated_rows(rng):
     assert np.array_equal(oracle.mla_decode(q, kv, qo, kvp, kv_indices=idx)[0], oracle.mla_decode(q, dup, qo, kvp)[0])
 
 
+@pytest.mark.parametrize("page_size", [2, 16, 64])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+def test_pages_equal_contiguous_rows(kv_dtype, page_size):
+    # pages of page_size rows: each sequence's rows are written page by page
+    # (here, not by the generator) into pages drawn from a permutation of a
+    # larger buffer; the oracle reading them through the page lists gives
+    # exactly the contiguous result
+    w = synth.make_batch([5, 0, 40, 17, 64, 1], "bf16", kv_dtype, seed=17, q_lens=[1, 2, 2, 1, 1, 1])
+    P = page_size
+    rng = np.random.default_rng(99 + P)
+    lens = np.diff(np.asarray(w.kv_indptr, dtype=np.int64))
+    starts = [0]
+    for n in lens:
+        starts.append(starts[-1] + (int(n) + P - 1) // P)
+    npages = starts[-1] + 5
+    page_ids = rng.permutation(npages)[: starts[-1]].astype(np.int32)
+    kv = np.zeros((npages * P,) + w.kv.shape[1:], dtype=w.kv.dtype)
+    ks = np.zeros((npages * P,) + w.kv_scale.shape[1:], dtype=np.uint8) if kv_dtype == "mxfp4" else w.kv_scale
+    for b, n in enumerate(lens):
+        for i in range(int(n)):
+            dst = int(page_ids[starts[b] + i // P]) * P + i % P
+            kv[dst] = w.kv[int(w.kv_indptr[b]) + i]
+            if kv_dtype == "mxfp4":
+                ks[dst] = w.kv_scale[int(w.kv_indptr[b]) + i]
+    a, la = oracle.decode_workload(w)
+    b_, lb = oracle.mla_decode(w.q, kv, w.qo_indptr, w.kv_indptr, q_dtype=w.q_dtype, kv_dtype=kv_dtype,
+                               q_scale=w.q_scale, kv_scale=ks, sm_scale=w.sm_scale, kv_indices=page_ids,
+                               kv_page_indptr=np.array(starts, dtype=np.int32), page_size=P)
+    assert np.array_equal(a, b_, equal_nan=True) and np.array_equal(la, lb, equal_nan=True)
+    # and the generator's paged layout reads back the same
+    pw = synth.page_workload(w, seed=18, spare_rows=3 * P, page_size=P)
+    assert pw.total_kv == w.total_kv and pw.kv_rows % P == 0
+    c, lc = oracle.decode_workload(pw)
+    assert np.array_equal(a, c, equal_nan=True) and np.array_equal(la, lc, equal_nan=True)
+
+
+def test_pages_bigger_than_every_sequence(rng):
+    # one page per sequence holding all its rows at its start: page p of P rows
+    # is rows [p * P, p * P + len) of the buffer
+    q, kv, qo, kvp = _rand_batch(rng, [6, 3])
+    P = 8
+    buf = np.zeros((3 * P,) + kv.shape[1:], dtype=kv.dtype)
+    buf[2 * P: 2 * P + 6] = kv[0:6]
+    buf[0:3] = kv[6:9]
+    out, _ = oracle.mla_decode(q, buf, qo, kvp, kv_indices=np.array([2, 0], dtype=np.int32),
+                               kv_page_indptr=np.array([0, 1, 2], dtype=np.int32), page_size=P)
+    assert np.array_equal(out, oracle.mla_decode(q, kv, qo, kvp)[0])
+
+
 # ----------------------------------------------------------------- quantised formats
 
 def test_fp8_kv_folding_identity(rng):

@@ -38,8 +38,10 @@ MUTANTS = {
     "q_head_stride": ("const int64_t base = (t * p->num_heads + h) * (int64_t)D;",
                       "const int64_t base = (t * p->num_heads) * (int64_t)D + h;"),
     "normalisation_dropped": ("for (int v = 0; v < V; ++v) out[v] /= l;", ""),
-    "paged_index_ignored": ("const int64_t row = sh->kv_indices ? (int64_t)sh->kv_indices[j0 + j] : j0 + j;",
-                            "const int64_t row = j0 + j;"),
+    "paged_index_ignored": ("else if (sh->kv_indices)\n        row = sh->kv_indices[j0 + j];", ""),
+    "page_offset_dropped": ("* sh->page_size + j % sh->page_size;", "* sh->page_size;"),
+    "page_list_start_ignored": ("sh->kv_indices[sh->kv_page_indptr[b] + j / sh->page_size]",
+                                "sh->kv_indices[j / sh->page_size]"),
     "soft_cap_outer_factor_dropped": ("scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);",
                                       "scores[j] = tanh(scores[j] / p->logit_cap);"),
     "soft_cap_before_sm_scale": ("scores[j] = p->sm_scale * dot;\n    if (p->logit_cap > 0.0) scores[j] = p->logit_cap * tanh(scores[j] / p->logit_cap);",
@@ -148,6 +150,21 @@ def pin_battery(lib):
     o2, _ = oracle.mla_decode(qb, kb, qo, kvp, lib=lib)
     if not np.array_equal(o, o2):
         failed.append("paged_permutation")
+
+    # pages of 4 rows: each sequence's rows laid page by page into pages drawn
+    # from a permutation, read back in CSR order
+    P = 4
+    lens = np.diff(np.asarray(kvp, dtype=np.int64))
+    starts = np.concatenate([[0], np.cumsum((lens + P - 1) // P)]).astype(np.int32)
+    npages = int(starts[-1]) + 3
+    page_ids = rng.permutation(npages)[: int(starts[-1])].astype(np.int32)
+    paged = np.zeros((npages * P,) + kb.shape[1:], dtype=kb.dtype)
+    for b in range(lens.shape[0]):
+        for i in range(int(lens[b])):
+            paged[int(page_ids[starts[b] + i // P]) * P + i % P] = kb[int(kvp[b]) + i]
+    o, _ = oracle.mla_decode(qb, paged, qo, kvp, lib=lib, kv_indices=page_ids, kv_page_indptr=starts, page_size=P)
+    if not np.array_equal(o, o2):
+        failed.append("pages_of_four")
 
     # split recombination of LSE-weighted pieces
     qr = np.repeat(qb[1:2], 3, axis=0)
