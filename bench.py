@@ -59,7 +59,9 @@ def _args():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--logit-cap", type=float, default=0.0, help="> 0: soft-cap the scaled scores")
     ap.add_argument("--paged", action="store_true",
-                    help="paged KV, page size 1: rows scattered over a buffer 1/8 larger by a random permutation")
+                    help="paged KV: rows (or pages, see --page-size) scattered over a buffer 1/8 larger by a "
+                         "random permutation")
+    ap.add_argument("--page-size", type=int, default=1, help="with --paged: rows per page (a power of two)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query rows per sequence (multi-token prediction / speculative decoding)")
     ap.add_argument("--rows-per-split", type=int, default=0)
@@ -143,8 +145,10 @@ class Timed:
         self.w = synth.make_workload(name, threads=threads, q_len=q_len)
         self.w.logit_cap = float(getattr(args, "logit_cap", 0.0))
         if getattr(args, "paged", False):
-            self.w = synth.page_workload(self.w, seed=99, spare_rows=self.w.total_kv // 8, threads=threads)
-            self.name += "_paged"
+            ps = int(getattr(args, "page_size", 1))
+            self.w = synth.page_workload(self.w, seed=99, spare_rows=self.w.total_kv // 8, threads=threads,
+                                         page_size=ps)
+            self.name += "_paged" if ps == 1 else f"_pages{ps}"
         self.t_gen = time.perf_counter() - t
         self.kv_bytes = self.w.kv_bytes()
         self.rows = int(self.w.kv_indptr[-1] - self.w.kv_indptr[0])
@@ -221,6 +225,7 @@ class Timed:
         d = mla.mla_decode_plan_describe(self.plan)
         return {"workload": self.name, "batch_size": self.spec["bs"], "kv_len": self.spec["kv_len"],
                 "q_len": self.q_len, "logit_cap": self.w.logit_cap, "paged": self.w.kv_indices is not None,
+                "page_size": int(getattr(self.w, "page_size", 1)),
                 "q_dtype": self.w.q_dtype, "kv_dtype": self.w.kv_dtype, "kv_rows": self.rows,
                 "kv_bytes": self.kv_bytes, "kv_copies_rotated": self.ncopy, "num_splits": d["num_splits"],
                 "rows_per_split": d["rows_per_split"], "stage2": bool(d["stage2"])}

@@ -72,12 +72,16 @@ typedef struct mla_problem {
                          logit_cap * tanh(s / logit_cap) before the softmax - the logit_cap
                          argument of the library decode call on submission 753817's page,
                          read as the usual soft-cap (the page passes 0.0) */
-  int32_t kv_paged;   /* 0: sequence b's KV rows are rows [kv_indptr[b], kv_indptr[b+1]) of kv;
-                         1: paged KV with page size 1 (the layout of the library decode call
-                         on submission 753817's page, page_size 1 with kv_indices): CSR row j
-                         is row kv_indices[j] of kv, and runs go through the _paged entry
-                         points.  Any KV format (MXFP4 scale rows are indexed like
-                         their rows) */
+  int32_t kv_paged;   /* 0: sequence b's KV rows are rows [kv_indptr[b], kv_indptr[b+1]) of kv.
+                         P >= 1, a power of two up to 65536: paged KV with pages of P rows
+                         (the kv_indices / page_size arguments of the library decode call on
+                         submission 753817's page, which passes page_size 1); runs go
+                         through the _paged entry points.  P = 1: CSR row j is row
+                         kv_indices[j] of kv.  P > 1: kv_indices lists pages, sequence b's
+                         from entry kv_page_indptr[b] on, and row i of sequence b (i from
+                         0) is row kv_indices[kv_page_indptr[b] + i / P] * P + i % P of kv.
+                         Any KV format (MXFP4 scale rows are indexed like their rows).
+                         Other values: MLA_ERR_INVALID_ARG */
 } mla_problem;
 
 /* Optional planner overrides (NULL = planner's choice for every field). */
@@ -159,28 +163,36 @@ mla_status mla_decode_run(const mla_plan* plan, const void* q, const float* q_sc
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * mla_decode_run for a plan made with kv_paged = 1.  The arguments are those of
- * mla_decode_run, with total_kv counting CSR rows, plus:
+ * mla_decode_run for a plan made with kv_paged = P >= 1.  The arguments are
+ * those of mla_decode_run, with total_kv counting CSR rows, plus:
  *   kv_rows    rows of the kv buffer ([kv_rows][576] bf16 or fp8 codes, [kv_rows][288]
  *              MXFP4 bytes with kv_scale [kv_rows][18]); at most 0xFFFFF000 bytes of
  *              rows (larger buffers: MLA_ERR_UNSUPPORTED).
- *   kv_indices device int32 [total_kv], 4-byte aligned: CSR row j of the plan is
- *              row kv_indices[j] of kv.  An index outside [0, kv_rows) gives
- *              undefined output for its sequence, but every read stays inside the
- *              kv buffer (reads past it return zero).
- * A contiguous plan, or a NULL kv_indices, is MLA_ERR_INVALID_ARG (and a paged
- * plan passed to mla_decode_run or mla_decode_split is too).
+ *   kv_indices device int32, 4-byte aligned.  P = 1: [total_kv] entries, CSR row j
+ *              of the plan is row kv_indices[j] of kv.  P > 1: page numbers, at
+ *              least kv_page_indptr[batch_size] entries; page p is rows
+ *              [p * P, p * P + P) of kv.  An index outside the buffer gives
+ *              undefined output for its sequence, but every KV read stays inside
+ *              the kv buffer (reads past it return zero).
+ *   kv_page_indptr  P > 1: device int32 [batch_size + 1], 4-byte aligned: sequence
+ *              b's pages are kv_indices[kv_page_indptr[b] ..], ceil(len_b / P) of
+ *              them (len_b = kv_indptr[b+1] - kv_indptr[b]).  The caller keeps
+ *              every listed entry inside kv_indices; a decreasing pair reads its
+ *              sequence as page 0.  P = 1: NULL.
+ * A contiguous plan, a NULL kv_indices, or a kv_page_indptr that does not match
+ * P is MLA_ERR_INVALID_ARG (and a paged plan passed to mla_decode_run or
+ * mla_decode_split is too).
  */
 mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
                                 const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
-                                const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                const int32_t* kv_page_indptr, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage 1 alone of mla_decode_run_paged (stage 2 is mla_decode_merge, unchanged). */
 mla_status mla_decode_split_paged(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
                                   const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
-                                  const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  const int32_t* kv_page_indptr, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                  void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The two stages of mla_decode_run as separate calls, for callers that put

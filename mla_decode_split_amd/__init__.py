@@ -67,9 +67,9 @@ def _lib_handle():
         lib.mla_decode_run.restype = i32
         lib.mla_decode_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_split.restype = i32
-        lib.mla_decode_run_paged.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+        lib.mla_decode_run_paged.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_run_paged.restype = i32
-        lib.mla_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+        lib.mla_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_split_paged.restype = i32
         lib.mla_decode_merge.argtypes = [vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_merge.restype = i32
@@ -179,26 +179,27 @@ def mla_decode_split(plan: Plan, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr,
         raise MlaError(st, "mla_decode_split")
 
 
-def mla_decode_run_paged(plan: Plan, q, q_scale, kv, kv_scale, kv_rows: int, kv_indices, qo_indptr, kv_indptr, out,
-                         workspace, workspace_bytes: int | None = None, stream=None) -> None:
+def mla_decode_run_paged(plan: Plan, q, q_scale, kv, kv_scale, kv_rows: int, kv_indices, kv_page_indptr, qo_indptr,
+                         kv_indptr, out, workspace, workspace_bytes: int | None = None, stream=None) -> None:
     lib = _lib_handle()
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     st = lib.mla_decode_run_paged(plan.handle, _addr(q), _addr(q_scale), _addr(kv), _addr(kv_scale), int(kv_rows),
-                                  _addr(kv_indices), _addr(qo_indptr), _addr(kv_indptr), _addr(out), _addr(workspace),
-                                  workspace_bytes, _stream(stream))
+                                  _addr(kv_indices), _addr(kv_page_indptr), _addr(qo_indptr), _addr(kv_indptr),
+                                  _addr(out), _addr(workspace), workspace_bytes, _stream(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_run_paged")
 
 
-def mla_decode_split_paged(plan: Plan, q, q_scale, kv, kv_scale, kv_rows: int, kv_indices, qo_indptr, kv_indptr,
-                           out, workspace, workspace_bytes: int | None = None, stream=None) -> None:
+def mla_decode_split_paged(plan: Plan, q, q_scale, kv, kv_scale, kv_rows: int, kv_indices, kv_page_indptr,
+                           qo_indptr, kv_indptr, out, workspace, workspace_bytes: int | None = None,
+                           stream=None) -> None:
     lib = _lib_handle()
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     st = lib.mla_decode_split_paged(plan.handle, _addr(q), _addr(q_scale), _addr(kv), _addr(kv_scale), int(kv_rows),
-                                    _addr(kv_indices), _addr(qo_indptr), _addr(kv_indptr), _addr(out),
-                                    _addr(workspace), workspace_bytes, _stream(stream))
+                                    _addr(kv_indices), _addr(kv_page_indptr), _addr(qo_indptr), _addr(kv_indptr),
+                                    _addr(out), _addr(workspace), workspace_bytes, _stream(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_split_paged")
 

@@ -46,9 +46,12 @@
 //   CAP   scaled scores soft-capped as cap * tanh(s / cap) before the softmax
 //         (the logit_cap argument of the library call on submission 753817's
 //         page, which passes 0.0);
-//   PAGED page size 1: CSR row j is row kv_indices[j] of the buffer (the
-//         kv_indices / page_size 1 layout of that call); wave 3 stages each
-//         tile's row indices in LDS, waves 0-2 gather the rows.
+//   PAGED paged KV (the kv_indices / page_size arguments of that call): with
+//         page size 1 CSR row j is row kv_indices[j] of the buffer; with page
+//         size P = 2^k, kv_indices lists pages and row i of sequence b is row
+//         i mod P of page kv_indices[kv_page_indptr[b] + i div P].  Wave 3
+//         stages each tile's index entries in LDS (with pages it turns them
+//         into row numbers there), waves 0-2 gather the rows.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -601,8 +604,20 @@ struct SplitParams {
   int32_t rows_per_wg;
   float sm_scale;
   float logit_cap;  // > 0: scaled scores soft-capped as cap * tanh(s / cap)
-  const int32_t* kv_indices;  // paged KV: CSR row j is row kv_indices[j] of kv
-  int64_t kv_rows;            // paged KV: rows of the kv buffer
+  const int32_t* kv_indices;      // paged KV: row or page indices
+  int64_t kv_rows;                // paged KV: rows of the kv buffer
+  const int32_t* kv_page_indptr;  // pages (page_shift > 0): sequence b's page list starts
+                                  // at kv_indices[kv_page_indptr[b]]
+  int32_t page_shift;             // paged KV: log2 of the page size
+};
+
+// Where a piece's index entries start in kv_indices (base), how many may be
+// read from there (count), and the piece's first row within its sequence
+// (jj0; 0 with page size 1, where the entries follow the CSR rows).
+struct PageSpan {
+  int64_t base;
+  int64_t count;
+  int32_t jj0;
 };
 
 // Query operand of S^T = K Q^T for the dims this wave multiplies.  The four
@@ -1111,7 +1126,8 @@ template <int QF, int KF, int QL, bool CAP, bool PAGED>
 __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf, int32_t* idxring,
                             uint8_t* dtab,
                             const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow0, int nq, int64_t r0,
-                            int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows) {
+                            int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows,
+                            PageSpan ps) {
   using G = Geom<KF>;
   using DM = Dma<KF, PAGED>;
   constexpr int NS = Ring<KF, QL, PAGED>::kStages;
@@ -1134,7 +1150,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   const i32x4 rk = make_rsrc(kv_base, (uint32_t)std::min<uint64_t>(kv_avail, 0xFFFFF000ull));
   i32x4 ri = rk;
   if constexpr (PAGED)
-    ri = make_rsrc(p.kv_indices + r0, (uint32_t)std::min<uint64_t>((uint64_t)(p.total_kv - r0) * 4, 0xFFFFF000ull));
+    ri = make_rsrc(p.kv_indices + ps.base, (uint32_t)std::min<uint64_t>((uint64_t)ps.count * 4, 0xFFFFF000ull));
   int64_t sbase = 0;
   i32x4 rs = rk;
   if constexpr (KF == DT_MXFP4) {
@@ -1192,9 +1208,20 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   // Paged KV: wave 3 stages the physical row indices of tile t (32 lanes, 4
   // bytes each) into index slot t % kIdxSlots, kIdxLead tiles ahead of the
   // tile whose DMA needs them; waves 0-2 read them when they issue that DMA.
+  // With pages the entry of tile row r is that of the row's page.
   auto stage_idx = [&](int t) {
     const uint32_t base = uniform(lds_addr(idxring + (t % kIdxSlots) * kTile));
-    if (lane < kTile) dma4(ri, base, (uint32_t)(t * kTile * 4) + 4 * lane);
+    if (lane < kTile) dma4(ri, base, 4u * ((uint32_t)(ps.jj0 + t * kTile + lane) >> p.page_shift));
+  };
+  // Pages: once tile t's entries are in LDS, wave 3 replaces each page number
+  // by its row's number (page * P + the row's place in the page) before the
+  // barrier that publishes them.
+  auto pages_to_rows = [&](int t) {
+    if (PAGED && p.page_shift && wd == 3 && lane < kTile) {
+      int32_t* e = idxring + (t % kIdxSlots) * kTile + lane;
+      const uint32_t in_page = (uint32_t)(ps.jj0 + t * kTile + lane) & ((1u << p.page_shift) - 1u);
+      *e = (int32_t)(((uint32_t)*e << p.page_shift) | in_page);
+    }
   };
   if (PAGED && wd == 3)
     for (int t = 0; t <= NS - 2 + kIdxLead; ++t) stage_idx(t);
@@ -1204,11 +1231,14 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   for (int t = 0; t < QW; ++t) qop[t].fetch(p.q, qrow0 + std::min(tb + t, nq - 1), lane, w);
 #pragma unroll
   for (int t = 0; t < QW; ++t) qop[t].arrive();
+  const int pro = std::min(NS - 1, ntiles);
   if constexpr (PAGED) {
-    if (wd == 3) wait_vmcnt<0>();  // the staged indices are in LDS
+    if (wd == 3) {
+      wait_vmcnt<0>();  // the staged indices are in LDS
+      for (int t = 0; t < pro; ++t) pages_to_rows(t);
+    }
     lds_barrier();
   }
-  const int pro = std::min(NS - 1, ntiles);
   for (int t = 0; t < pro; ++t) issue_tile(t);
   // per-token head maxima past the sequence counts at the start of xchg
 #pragma unroll
@@ -1244,6 +1274,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   auto idx_step = [&](int i) {
     if (PAGED && wd == 3) {
       wait_vmcnt<kIdxLead - 1>();
+      pages_to_rows(i + NS - 1);
       stage_idx(i + NS - 1 + kIdxLead);
     }
   };
@@ -1428,8 +1459,16 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
     const int64_t r0 = std::max(s, lo), r1 = std::min(e, hi);
     if (r0 >= r1) continue;
     const int32_t slot = piece_slot(s, e, lo, hi, gi);
+    PageSpan ps{r0, p.total_kv - r0, 0};
+    if (PAGED && p.page_shift) {
+      const int32_t pb_raw = p.kv_page_indptr[b], pe_raw = p.kv_page_indptr[b + 1];
+      const int64_t pb = uniform(pb_raw), pe = uniform(pe_raw);
+      // a page list that cannot be read is read as empty (all pages 0)
+      const bool ok = pb >= 0 && pe >= pb;
+      ps = PageSpan{ok ? pb : 0, ok ? pe - pb : 0, (int32_t)(r0 - s)};
+    }
     split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
-                            r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg);
+                            r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg, ps);
     lds_barrier();  // the next piece refills the ring
   }
 }
@@ -1723,7 +1762,8 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   // query rows per sequence: one, or up to max_q_len (2 or 4 kernels; 3 runs on the 4-token one)
   if (pr->max_q_len < 0 || pr->max_q_len > 4) return MLA_ERR_UNSUPPORTED;
   if (!(pr->logit_cap >= 0.f) || !(pr->logit_cap < INFINITY)) return MLA_ERR_INVALID_ARG;
-  if (pr->kv_paged != 0 && pr->kv_paged != 1) return MLA_ERR_INVALID_ARG;
+  // 0: contiguous; P = 2^k in [1, 65536]: paged with pages of P rows
+  if (pr->kv_paged < 0 || pr->kv_paged > 65536 || (pr->kv_paged & (pr->kv_paged - 1))) return MLA_ERR_INVALID_ARG;
   const int ql = pr->max_q_len <= 1 ? 1 : pr->max_q_len == 2 ? 2 : 4;
   if (ql == 1 && pr->total_q != pr->batch_size) return MLA_ERR_UNSUPPORTED;  // one query token per sequence
   if (ql > 1 && (pr->total_q < 1 || (int64_t)pr->total_q > (int64_t)pr->batch_size * pr->max_q_len))
@@ -1871,14 +1911,18 @@ mla_status mla_decode_plan_merge_slots(const mla_plan* pl, const int32_t* ind, i
 namespace {
 
 // Validates the run arguments and fills the kernel parameter blocks.
-// kv_indices / kv_rows: the paged entry points (kv_indices != NULL) with a
-// paged plan, the others (NULL) with a contiguous one.
+// kv_indices / kv_rows / kv_page_indptr: the paged entry points (kv_indices
+// != NULL) with a paged plan, the others (NULL) with a contiguous one; the page
+// lists (kv_page_indptr) with pages of more than one row only.
 mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, const void* kv, const void* kv_scale,
-                   const int32_t* kv_indices, int64_t kv_rows, const int32_t* qo_indptr, const int32_t* kv_indptr,
-                   void* out, void* workspace, size_t workspace_bytes, SplitParams* sp, MergeParams* mp) {
+                   const int32_t* kv_indices, int64_t kv_rows, const int32_t* kv_page_indptr,
+                   const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
+                   size_t workspace_bytes, SplitParams* sp, MergeParams* mp) {
   if (!pl || !q || !kv || !qo_indptr || !kv_indptr || !out) return MLA_ERR_INVALID_ARG;
   const mla_problem& pr = pl->prob;
   if ((kv_indices != nullptr) != (pr.kv_paged != 0)) return MLA_ERR_INVALID_ARG;
+  if ((kv_page_indptr != nullptr) != (pr.kv_paged > 1)) return MLA_ERR_INVALID_ARG;
+  if (kv_page_indptr && ((uintptr_t)kv_page_indptr & 3u)) return MLA_ERR_INVALID_ARG;
   if (kv_indices) {
     const int64_t row_bytes = pr.kv_dtype == DT_BF16 ? 2 * kQK : pr.kv_dtype == DT_FP8 ? kQK : kQK / 2;
     if (((uintptr_t)kv_indices & 3u) || kv_rows < 1) return MLA_ERR_INVALID_ARG;
@@ -1907,6 +1951,8 @@ mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, cons
   sp->logit_cap = pr.logit_cap;
   sp->kv_indices = kv_indices;
   sp->kv_rows = kv_rows;
+  sp->kv_page_indptr = kv_page_indptr;
+  sp->page_shift = pr.kv_paged > 1 ? __builtin_ctz((unsigned)pr.kv_paged) : 0;
   mp->part_o = sp->part_o;
   mp->part_lse = sp->part_lse;
   mp->qo_indptr = qo_indptr;
@@ -1961,7 +2007,7 @@ mla_status mla_decode_run(const mla_plan* pl, const void* q, const float* q_scal
                           void* workspace, size_t workspace_bytes, void* stream) {
   SplitParams sp;
   MergeParams mp;
-  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, nullptr, 0, qo_indptr, kv_indptr, out, workspace,
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, nullptr, 0, nullptr, qo_indptr, kv_indptr, out, workspace,
                          workspace_bytes, &sp, &mp);
   if (s != MLA_OK) return s;
   s = launch_split_stage(pl, sp, (hipStream_t)stream);
@@ -1971,13 +2017,13 @@ mla_status mla_decode_run(const mla_plan* pl, const void* q, const float* q_scal
 
 mla_status mla_decode_run_paged(const mla_plan* pl, const void* q, const float* q_scale, const void* kv,
                                 const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
-                                const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                const int32_t* kv_page_indptr, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!kv_indices) return MLA_ERR_INVALID_ARG;
   SplitParams sp;
   MergeParams mp;
-  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, kv_indices, kv_rows, qo_indptr, kv_indptr, out, workspace,
-                         workspace_bytes, &sp, &mp);
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, kv_indices, kv_rows, kv_page_indptr, qo_indptr, kv_indptr,
+                         out, workspace, workspace_bytes, &sp, &mp);
   if (s != MLA_OK) return s;
   s = launch_split_stage(pl, sp, (hipStream_t)stream);
   if (s != MLA_OK) return s;
@@ -1986,13 +2032,13 @@ mla_status mla_decode_run_paged(const mla_plan* pl, const void* q, const float* 
 
 mla_status mla_decode_split_paged(const mla_plan* pl, const void* q, const float* q_scale, const void* kv,
                                   const void* kv_scale, int64_t kv_rows, const int32_t* kv_indices,
-                                  const int32_t* qo_indptr, const int32_t* kv_indptr, void* out, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  const int32_t* kv_page_indptr, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!kv_indices) return MLA_ERR_INVALID_ARG;
   SplitParams sp;
   MergeParams mp;
-  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, kv_indices, kv_rows, qo_indptr, kv_indptr, out, workspace,
-                         workspace_bytes, &sp, &mp);
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, kv_indices, kv_rows, kv_page_indptr, qo_indptr, kv_indptr,
+                         out, workspace, workspace_bytes, &sp, &mp);
   if (s != MLA_OK) return s;
   return launch_split_stage(pl, sp, (hipStream_t)stream);
 }
@@ -2002,7 +2048,7 @@ mla_status mla_decode_split(const mla_plan* pl, const void* q, const float* q_sc
                             void* workspace, size_t workspace_bytes, void* stream) {
   SplitParams sp;
   MergeParams mp;
-  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, nullptr, 0, qo_indptr, kv_indptr, out, workspace,
+  mla_status s = prepare(pl, q, q_scale, kv, kv_scale, nullptr, 0, nullptr, qo_indptr, kv_indptr, out, workspace,
                          workspace_bytes, &sp, &mp);
   if (s != MLA_OK) return s;
   return launch_split_stage(pl, sp, (hipStream_t)stream);

@@ -27,6 +27,8 @@ class DeviceBatch:
     max_q_len: int
     logit_cap: float
     kv_indices: torch.Tensor | None  # paged KV (page size 1): CSR row j is kv row kv_indices[j]
+    kv_page_indptr: torch.Tensor | None  # pages of page_size > 1 rows: sequence b's page list start
+    page_size: int                   # paged KV: rows per page
     total_kv_rows: int               # CSR rows (kv rows when not paged)
     q_dtype: str
     kv_dtype: str
@@ -75,6 +77,9 @@ def upload(w, device="cuda") -> DeviceBatch:
                        logit_cap=float(getattr(w, "logit_cap", 0.0)),
                        kv_indices=None if getattr(w, "kv_indices", None) is None
                        else _to_dev(np.asarray(w.kv_indices, dtype=np.int32), device),
+                       kv_page_indptr=None if getattr(w, "kv_page_indptr", None) is None
+                       else _to_dev(np.asarray(w.kv_page_indptr, dtype=np.int32), device),
+                       page_size=int(getattr(w, "page_size", 1)),
                        total_kv_rows=int(w.total_kv),
                        q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, sm_scale=float(w.sm_scale))
 
@@ -83,7 +88,7 @@ def plan_for(batch: DeviceBatch, rows_per_split: int = 0, wgs_per_cu: int = 0, u
              num_cus: int = 0) -> Plan:
     prob = make_problem(batch.batch_size, batch.total_kv, batch.q_dtype, batch.kv_dtype, total_q=batch.total_q,
                         sm_scale=batch.sm_scale, num_cus=num_cus, max_q_len=batch.max_q_len,
-                        logit_cap=batch.logit_cap, kv_paged=batch.kv_indices is not None)
+                        logit_cap=batch.logit_cap, kv_paged=batch.page_size if batch.kv_indices is not None else 0)
     opts = mla_plan_options(rows_per_split, wgs_per_cu) if (rows_per_split or wgs_per_cu) else None
     return mla_decode_plan(prob, opts, batch.kv_indptr_host if use_host_indptr else None)
 
@@ -104,7 +109,8 @@ def run(plan: Plan, batch: DeviceBatch, out: torch.Tensor | None = None, workspa
         workspace = workspace_for(plan, batch.q.device)
     if batch.kv_indices is not None:
         mla_decode_run_paged(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.kv_rows, batch.kv_indices,
-                             batch.qo_indptr, batch.kv_indptr, out, workspace, workspace.numel(), stream)
+                             batch.kv_page_indptr, batch.qo_indptr, batch.kv_indptr, out, workspace, workspace.numel(),
+                             stream)
     else:
         mla_decode_run(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.qo_indptr, batch.kv_indptr, out,
                        workspace, workspace.numel(), stream)
@@ -114,8 +120,8 @@ def run(plan: Plan, batch: DeviceBatch, out: torch.Tensor | None = None, workspa
 def run_split(plan: Plan, batch: DeviceBatch, out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     if batch.kv_indices is not None:
         mla_decode_split_paged(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.kv_rows,
-                               batch.kv_indices, batch.qo_indptr, batch.kv_indptr, out, workspace, workspace.numel(),
-                               stream)
+                               batch.kv_indices, batch.kv_page_indptr, batch.qo_indptr, batch.kv_indptr, out,
+                               workspace, workspace.numel(), stream)
     else:
         mla_decode_split(plan, batch.q, batch.q_scale, batch.kv, batch.kv_scale, batch.qo_indptr, batch.kv_indptr,
                          out, workspace, workspace.numel(), stream)

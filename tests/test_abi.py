@@ -251,16 +251,17 @@ def test_paged_plans(kv_dtype, q_len):
 
 def test_paged_argument_errors_before_any_launch():
     """Every call below fails host-side validation (fake, never dereferenced addresses)."""
-    prob = mla.make_problem(4, 100, num_cus=256, kv_paged=2)
-    assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG
+    for bad in (3, -1, 12, 1 << 17):  # page sizes: powers of two up to 65536
+        prob = mla.make_problem(4, 100, num_cus=256, kv_paged=bad)
+        assert _status(mla.mla_decode_plan, prob) == mla.MLA_ERR_INVALID_ARG
     A = 1 << 20
     ind = _indptr([32, 32])
     flat = _plan(2, 64, kv="fp8", ind=ind)
     paged = mla.mla_decode_plan(mla.make_problem(2, 64, "bf16", "fp8", num_cus=256, kv_paged=1), None, ind)
     n = paged.workspace_bytes
 
-    def run_paged(plan, kv_rows=1000, kv_indices=A):
-        return _status(mla.mla_decode_run_paged, plan, A, A, A, A, kv_rows, kv_indices, A, A, A, A, n)
+    def run_paged(plan, kv_rows=1000, kv_indices=A, kv_page_indptr=None):
+        return _status(mla.mla_decode_run_paged, plan, A, A, A, A, kv_rows, kv_indices, kv_page_indptr, A, A, A, A, n)
 
     assert run_paged(flat) == mla.MLA_ERR_INVALID_ARG                    # contiguous plan
     assert run_paged(paged, kv_indices=None) == mla.MLA_ERR_INVALID_ARG
@@ -269,7 +270,13 @@ def test_paged_argument_errors_before_any_launch():
     assert run_paged(paged, kv_rows=1 << 23) == mla.MLA_ERR_UNSUPPORTED   # > 4 GB of fp8 rows
     assert _status(mla.mla_decode_run, paged, A, A, A, A, A, A, A, A, n) == mla.MLA_ERR_INVALID_ARG
     assert _status(mla.mla_decode_split, paged, A, A, A, A, A, A, A, A, n) == mla.MLA_ERR_INVALID_ARG
-    assert _status(mla.mla_decode_split_paged, flat, A, A, A, A, 1000, A, A, A, A, A, n) == mla.MLA_ERR_INVALID_ARG
+    assert _status(mla.mla_decode_split_paged, flat, A, A, A, A, 1000, A, None, A, A, A, A, n) == mla.MLA_ERR_INVALID_ARG
+    assert run_paged(paged, kv_page_indptr=A) == mla.MLA_ERR_INVALID_ARG   # page lists with page size 1
+    pages = mla.mla_decode_plan(mla.make_problem(2, 64, "bf16", "fp8", num_cus=256, kv_paged=16), None, ind)
+    assert run_paged(pages) == mla.MLA_ERR_INVALID_ARG                       # page size 16 without page lists
+    assert run_paged(pages, kv_page_indptr=A + 2) == mla.MLA_ERR_INVALID_ARG  # not 4-byte aligned
+    assert _status(mla.mla_decode_split_paged, pages, A, A, A, A, 1000, A, None, A, A, A, A, n) == \
+        mla.MLA_ERR_INVALID_ARG
 
 
 def test_plan_destroy_accepts_null():

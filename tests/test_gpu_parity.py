@@ -324,6 +324,30 @@ def test_paged_two_query_rows(kv_dtype, cap):
     _paged_equals_contiguous(w, pw, rows_per_split=96, what=f"paged q2 cap={cap} kv={kv_dtype}")
 
 
+@pytest.mark.parametrize("page_size", [2, 16, 64, 256])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+def test_pages_of_several_rows(kv_dtype, page_size):
+    # pages of page_size rows listed per sequence: query rows 0-4, a cap and
+    # forced splits (pieces start inside pages), against the oracle and bitwise
+    # against contiguous KV
+    w = synth.make_batch([700, 0, 33, 1000, 1, 257], "bf16", kv_dtype, seed=201, name="pages",
+                         q_lens=[2, 1, 4, 0, 3, 1])
+    w.logit_cap = 2.0
+    pw = synth.page_workload(w, seed=202 + page_size, spare_rows=3 * page_size, page_size=page_size)
+    (_, _), plan, _ = _check_batch(pw, rows_per_split=96, what=f"pages of {page_size} rows, kv={kv_dtype}")
+    _paged_equals_contiguous(w, pw, rows_per_split=96, what=f"pages of {page_size} rows kv={kv_dtype}")
+
+
+def test_pages_full_size_sampled():
+    # bs 64, KV 8192 fp8 in pages of 16 rows, in the planner's launch
+    # configuration: sampled sequences against the oracle, the whole output
+    # bitwise against the contiguous run
+    w = synth.make_workload("bs64_kv8192_fp8")
+    pw = synth.page_workload(w, seed=211, spare_rows=w.total_kv // 8, page_size=16)
+    _check_batch(pw, seq_ids=[0, 1, 31, 63], poison=False, what="bs64 kv8192 fp8 pages of 16 (sampled)")
+    _paged_equals_contiguous(w, pw, what="bs64 kv8192 fp8 pages of 16")
+
+
 def test_paged_plan_without_host_indptr():
     w = synth.make_batch([100, 7, 900, 64], "bf16", "fp8", seed=171, name="paged-no-host")
     pw = synth.page_workload(w, seed=172, spare_rows=64)
