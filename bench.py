@@ -43,8 +43,8 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "b96f776fab646280b91f5ba45bc12fe2a19d12f60b3243c6b9823cb90f95349a",
-    "fetch_kib": 152179.3,
+    "source_sha256": "f49d9a821f17bb05dc53cf4b6b9bd48951301f56be0c367faa023478db8eb872",
+    "fetch_kib": 152171.7,
     "write_kib": 8224.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
