@@ -249,6 +249,20 @@ def test_paged_plans(kv_dtype, q_len):
     _check_cut(plan, ind)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+def test_page_sizes_share_the_paged_plan(kv_dtype):
+    # pages of any power-of-two size run the page-size-1 kernels: same cut,
+    # ring and residency
+    ind = _indptr([700, 33, 4000, 1])
+    base = mla.mla_decode_plan_describe(mla.mla_decode_plan(
+        mla.make_problem(4, int(ind[-1]), "bf16", kv_dtype, num_cus=256, kv_paged=1), None, ind))
+    for P in (2, 16, 64, 1024, 65536):
+        plan = mla.mla_decode_plan(mla.make_problem(4, int(ind[-1]), "bf16", kv_dtype, num_cus=256, kv_paged=P),
+                                   None, ind)
+        assert mla.mla_decode_plan_describe(plan) == base
+        _check_cut(plan, ind)
+
+
 def test_paged_argument_errors_before_any_launch():
     """Every call below fails host-side validation (fake, never dereferenced addresses)."""
     for bad in (3, -1, 12, 1 << 17):  # page sizes: powers of two up to 65536
