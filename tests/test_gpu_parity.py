@@ -299,6 +299,15 @@ def test_paged_edge_lengths(q_dtype, kv_dtype):
     _paged_equals_contiguous(w, pw, what=f"paged {q_dtype}/{kv_dtype}")
 
 
+@pytest.mark.parametrize("q_dtype,kv_dtype", PAGED_COMBOS)
+def test_pages_edge_lengths(q_dtype, kv_dtype):
+    # pages of 32 rows (one tile) at the edge lengths, every format pair
+    w = synth.make_batch(EDGE_LENGTHS, q_dtype, kv_dtype, seed=153, name="pages-edges")
+    pw = synth.page_workload(w, seed=154, spare_rows=777, page_size=32)
+    _check_batch(pw, what=f"pages of 32 {q_dtype}/{kv_dtype}")
+    _paged_equals_contiguous(w, pw, what=f"pages of 32 {q_dtype}/{kv_dtype}")
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("rows", [32, 96, 512])
 def test_paged_query_rows_cap_and_splits(kv_dtype, rows):
