@@ -81,3 +81,27 @@ def test_workload_shapes(name):
     assert w.kv_indptr[-1] == w.total_kv
     if spec["kv_len"] != "ragged":
         assert np.all(np.diff(w.kv_indptr) == spec["kv_len"])
+
+
+@pytest.mark.parametrize("page_size", [1, 4, 32])
+def test_page_layout_is_a_valid_scatter(page_size):
+    # every CSR row lands on its own buffer row, in whole pages listed per
+    # sequence, and the rows no sequence uses hold other data
+    w = synth.make_batch([70, 0, 33, 1, 128], "bf16", "mxfp4", seed=31)
+    pw = synth.page_workload(w, seed=32, spare_rows=40, page_size=page_size)
+    P = page_size
+    assert pw.total_kv == w.total_kv and pw.kv_rows % P == 0
+    lens = np.diff(w.kv_indptr.astype(np.int64))
+    if P == 1:
+        dest = pw.kv_indices.astype(np.int64)
+        assert pw.kv_page_indptr is None
+    else:
+        kpp = pw.kv_page_indptr.astype(np.int64)
+        assert np.array_equal(np.diff(kpp), (lens + P - 1) // P) and kpp[0] == 0
+        assert len(set(pw.kv_indices.tolist())) == pw.kv_indices.size  # no page shared
+        dest = np.concatenate([pw.kv_indices[kpp[b] + np.arange(n) // P].astype(np.int64) * P + np.arange(n) % P
+                               for b, n in enumerate(lens)])
+    assert dest.min() >= 0 and dest.max() < pw.kv_rows and np.unique(dest).size == dest.size
+    assert np.array_equal(pw.kv[dest], w.kv) and np.array_equal(pw.kv_scale[dest], w.kv_scale)
+    unused = np.setdiff1d(np.arange(pw.kv_rows), dest)
+    assert unused.size >= 40 and np.any(pw.kv[unused] != 0)
