@@ -1035,10 +1035,11 @@ __device__ inline void score_tile(uint8_t* st, uint8_t* pb, float* xchg, const Q
       if constexpr (CAP) v = cap.apply(v, t);
       ts[t].sv[blk] = (MASK && 16 * blk + 4 * g + w >= valid) ? -INFINITY : v;
     }
-    // the base-2 score is sv * c with c > 0
+    // the base-2 score is sv * c with c >= 0; a masked row's probability is 0
+    // by selection (with c = 0, a zero q or KV scale, -inf * c would be NaN)
     const float t0 = fmaf(ts[t].sv[0], c[t], -ws[t].m_run), t1 = fmaf(ts[t].sv[1], c[t], -ws[t].m_run);
-    ts[t].p[0] = __builtin_amdgcn_exp2f(t0);
-    ts[t].p[1] = __builtin_amdgcn_exp2f(t1);
+    ts[t].p[0] = (MASK && 4 * g + w >= valid) ? 0.f : __builtin_amdgcn_exp2f(t0);
+    ts[t].p[1] = (MASK && 16 + 4 * g + w >= valid) ? 0.f : __builtin_amdgcn_exp2f(t1);
     uint8_t* ps = p_ptr<KF>(st, pb, tb + t, lane);
     *(__bf16*)(ps + 2 * w) = (__bf16)ts[t].p[0];
     *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts[t].p[1];
@@ -1074,7 +1075,8 @@ __device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>&
       float mx = fmaxf(ts[t].sv[0], ts[t].sv[1]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      if (g == 0) *(float*)(max_ptr<KF, PAGED>(st, pb, tb + t, m) + 4 * w) = mx * c[t];
+      // a wave whose rows are all masked posts -inf (not -inf * c, NaN when c = 0)
+      if (g == 0) *(float*)(max_ptr<KF, PAGED>(st, pb, tb + t, m) + 4 * w) = mx == -INFINITY ? -INFINITY : mx * c[t];
     }
     lds_barrier();
 #pragma unroll
@@ -1088,8 +1090,8 @@ __device__ inline void finish_tile(uint8_t* st, uint8_t* pb, const LaneOffs<KF>&
       ws[t].l_run *= alpha;
 #pragma unroll
       for (int j = 0; j < 8; ++j) ws[t].acc[j] *= alpha;
-      ts[t].p[0] = __builtin_amdgcn_exp2f(fmaf(ts[t].sv[0], c[t], -ws[t].m_run));
-      ts[t].p[1] = __builtin_amdgcn_exp2f(fmaf(ts[t].sv[1], c[t], -ws[t].m_run));
+      ts[t].p[0] = (MASK && 4 * g + w >= valid) ? 0.f : __builtin_amdgcn_exp2f(fmaf(ts[t].sv[0], c[t], -ws[t].m_run));
+      ts[t].p[1] = (MASK && 16 + 4 * g + w >= valid) ? 0.f : __builtin_amdgcn_exp2f(fmaf(ts[t].sv[1], c[t], -ws[t].m_run));
       uint8_t* ps = p_ptr<KF>(st, pb, tb + t, lane);
       *(__bf16*)(ps + 2 * w) = (__bf16)ts[t].p[0];
       *(__bf16*)(ps + 8 + 2 * w) = (__bf16)ts[t].p[1];

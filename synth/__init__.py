@@ -256,6 +256,43 @@ def make_batch(lengths, q_dtype: str, kv_dtype: str, seed: int, name: str = "cus
                     meta={"seed": seed, "lengths": lengths, "q_lens": np.diff(qo_indptr)})
 
 
+def encode_batch(q: np.ndarray, kv: np.ndarray, qo_indptr, kv_indptr, q_dtype: str, kv_dtype: str,
+                 name: str = "encoded") -> Workload:
+    """A batch from given values instead of draws: fp32 q [total_q, 16, 576] and
+    kv [total_kv, 576] encoded into the storage formats the way make_batch
+    encodes its draws - bf16 round to nearest even; fp8 per tensor with scale =
+    fp32(amax) / 448 and codes RNE_E4M3(clamp(fp32(x / scale), +-448)); MXFP4
+    per 32-element block (shared exponent floor(log2 amax) - 2)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    kv = np.ascontiguousarray(kv, dtype=np.float32)
+    qo = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    ki = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+
+    def fp8(x):
+        amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+        scale = np.float32(max(amax, np.float32(1e-12)) / np.float32(448.0))
+        return encode_e4m3fn(np.clip(x / scale, -448.0, 448.0).astype(np.float32)), scale
+
+    q_scale = kv_scale = None
+    if q_dtype == "bf16":
+        qc = bf16_bits(q)
+    elif q_dtype == "fp8":
+        qc, q_scale = fp8(q)
+    else:
+        raise ValueError(q_dtype)
+    if kv_dtype == "bf16":
+        kvc = bf16_bits(kv)
+    elif kv_dtype == "fp8":
+        kvc, kv_scale = fp8(kv)
+    elif kv_dtype == "mxfp4":
+        kvc, kv_scale = encode_mxfp4(kv)
+    else:
+        raise ValueError(kv_dtype)
+    return Workload(name=name, q_dtype=q_dtype, kv_dtype=kv_dtype, q=qc.reshape(q.shape), q_scale=q_scale,
+                    kv=kvc, kv_scale=kv_scale, qo_indptr=qo, kv_indptr=ki,
+                    meta={"lengths": np.diff(ki), "q_lens": np.diff(qo)})
+
+
 def page_workload(w: Workload, seed: int, spare_rows: int = 0, threads: int | None = None,
                   page_size: int = 1) -> Workload:
     """The same batch with its KV rows scattered over a larger buffer (paged
