@@ -213,6 +213,24 @@ mla_status mla_decode_split(const mla_plan* plan, const void* q, const float* q_
 mla_status mla_decode_merge(const mla_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mla_decode_run for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, which is instead a static device
+ * array of 34 MiB (35,651,584 bytes) that the library holds on every device it
+ * runs on until the process ends.  Allocates nothing and frees nothing; the
+ * first call on a device looks the array's address up once.
+ *   Plans whose workspace_bytes exceed 34 MiB get MLA_ERR_UNSUPPORTED (with
+ *   mla_last_error_string() saying so); every plan the planner makes by
+ *   default for up to ~2.7e8 KV rows on a 256-CU device fits.
+ *   All calls on one device share the array, and nothing in it needs to start
+ *   at zero: calls that overlap on one device (concurrent streams, or threads)
+ *   race on it and give undefined output.  Calls ordered on one stream are safe.
+ */
+mla_status mla_decode_run_noalloc(const mla_plan* plan, const void* q, const float* q_scale, const void* kv,
+                                  const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                  void* out, void* stream);
+
 /* Free a plan (NULL is accepted). */
 void mla_decode_plan_destroy(mla_plan* plan);
 

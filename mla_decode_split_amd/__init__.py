@@ -71,6 +71,8 @@ def _lib_handle():
         lib.mla_decode_run_paged.restype = i32
         lib.mla_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_split_paged.restype = i32
+        lib.mla_decode_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.mla_decode_run_noalloc.restype = i32
         lib.mla_decode_merge.argtypes = [vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_merge.restype = i32
         lib.mla_decode_plan_destroy.argtypes = [vp]
@@ -166,6 +168,13 @@ def mla_decode_run(plan: Plan, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, o
                             _addr(kv_indptr), _addr(out), _addr(workspace), workspace_bytes, _stream(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode_run")
+
+
+def mla_decode_run_noalloc(plan: Plan, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, out, stream=None) -> None:
+    st = _lib_handle().mla_decode_run_noalloc(plan.handle, _addr(q), _addr(q_scale), _addr(kv), _addr(kv_scale),
+                                              _addr(qo_indptr), _addr(kv_indptr), _addr(out), _stream(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_decode_run_noalloc")
 
 
 def mla_decode_split(plan: Plan, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, out, workspace,

@@ -60,6 +60,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <type_traits>
 
@@ -1647,6 +1648,15 @@ __global__ __launch_bounds__(256) void mla_debug_stream_read_kernel(const u32x4*
 
 using namespace mla;
 
+// Workspace of mla_decode_run_noalloc: one static array per device, allocated
+// when the code object loads and held until the process ends.  34 MiB covers
+// the partial slots of every plan the planner makes by default on a 256-CU
+// part (at most 2 * 768 slots of one query row, or 2 * 512 of two, or 2 * 256
+// of four, plus their log-sum-exps) unless total_kv passes about 2.7e8 rows.
+// Host code never names it except to look up its device address.
+constexpr size_t kScratchBytes = size_t(34) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 struct mla_plan {
   mla_problem prob;
   int32_t rows_per_wg;
@@ -2087,6 +2097,55 @@ mla_status mla_debug_decode(int32_t kv_dtype, const void* codes, const void* sca
                      (const uint8_t*)codes, (const uint8_t*)scales, out, n);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the decode check");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` per device, looked up once per device (with that
+// device current) on the first mla_decode_run_noalloc call there.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mla_status scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the current device");
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_last_error, sizeof g_last_error, "device %d: at most %d devices are supported", dev, kMaxDevices);
+    return MLA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "looking up the static workspace");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_run_noalloc(const mla_plan* pl, const void* q, const float* q_scale, const void* kv,
+                                  const void* kv_scale, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
+                                  void* stream) {
+  if (!pl) return MLA_ERR_INVALID_ARG;
+  if (pl->ws_bytes > kScratchBytes) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "the plan needs %zu bytes of workspace; mla_decode_run_noalloc has %zu (use mla_decode_run)",
+             pl->ws_bytes, kScratchBytes);
+    return MLA_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  mla_status s = scratch_address(&ws);
+  if (s != MLA_OK) return s;
+  return mla_decode_run(pl, q, q_scale, kv, kv_scale, qo_indptr, kv_indptr, out, ws, kScratchBytes, stream);
 }
 
 mla_status mla_debug_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
