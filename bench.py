@@ -4,18 +4,21 @@ A step is one decode of the batch (mla_decode_run: the stage-1 split kernel,
 then the stage-2 LSE merge) over seeded synthetic inputs already resident in
 HBM.
 The default workload is bs=64, kv_len=8192, bf16 q, fp8 E4M3FN KV (the
-bs>=32 / kv=8192 / fp8 shape the bandwidth target is stated for).  The KV
-buffer is rotated over enough copies (>= 768 MB in total) that each call reads
-KV that is not resident in the 256 MB last-level cache: the bandwidth is HBM
-bandwidth, not cache bandwidth.
+bs>=32 / kv=8192 / fp8 shape the bandwidth target is stated for).  Every
+workload's KV buffer is rotated over enough copies (>= 768 MB in total, so
+163 copies of the 4.7 MB bs=4 batch) that each call reads KV that is not
+resident in the 256 MB last-level cache: the bandwidth is HBM bandwidth, not
+cache bandwidth.
 
 Prints one JSON line: value = KV bytes read per second over the timed steps
 (GB/s; K calls back to back between two synchronisations), plus per-call
 microseconds, the stage-1 kernel's roofline (its average launch duration from
 K stage-1 launches back to back between two HIP events on the launch stream)
-and the CPU oracle timed on a bounded sample of the same workload.  The plain
-read kernel runs first, over ~0.2 s, for the read ceiling; it also brings the
-device to its working clocks before the timed steps.
+and the CPU oracle timed on a bounded sample of the same workload.  The table
+of workloads gives the same figures for each of the five workloads (and the
+headline shape with two and four query rows), each with the oracle timed on a
+bounded sample of that workload.  A plain read kernel over one 1 GiB buffer
+(at most 200 launches) gives the read rate of this device as context.
 """
 from __future__ import annotations
 
@@ -68,17 +71,19 @@ def _args():
     ap.add_argument("--wgs-per-cu", type=int, default=0)
     ap.add_argument("--hot", action="store_true", help="no KV rotation (cache-resident numbers, secondary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU thread-seconds of each oracle sample")
     ap.add_argument("--only-headline", action="store_true", help="skip the per-workload table")
-    ap.add_argument("--read-ceiling-s", type=float, default=0.2,
-                    help="seconds of the plain read kernel for the read ceiling (0: skip it, e.g. under a "
-                         "counter-collecting profiler, where thousands of short launches are slow)")
+    ap.add_argument("--read-ceiling-s", type=float, default=0.03,
+                    help="seconds of the plain read kernel over one 1 GiB buffer (at most 200 launches; 0: skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MB (reference for HBM counters)")
     return ap.parse_args()
 
 
 def _host_threads() -> int:
+    """Threads for the oracle: the CPUs this process may run on, at most 16
+    (a one-GPU share of the GPU hosts here)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
@@ -86,24 +91,45 @@ def _host_threads() -> int:
     return max(1, min(16, n))
 
 
+def _cpu_description() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(w, kv_bytes_per_row: float, target_s: float) -> dict:
-    """The oracle, unchanged, on a bounded sample of the workload's sequences."""
+    """The oracle, unchanged, on a bounded sample of the workload's sequences:
+    about `target_s` thread-seconds on _host_threads() threads."""
     import oracle
 
     threads = _host_threads()
     lengths = np.diff(w.kv_indptr).astype(np.int64)
+    qo = np.diff(np.asarray(w.qo_indptr, dtype=np.int64))
     order = np.arange(len(lengths))
     # calibrate on one sequence, then take as many as fit the time budget
+    first = int(np.flatnonzero(lengths > 0)[0])
     t0 = time.perf_counter()
-    oracle.decode_workload(w, seq_ids=[int(order[0])], threads=1)
-    per_row = (time.perf_counter() - t0) / max(int(lengths[0]), 1)
-    budget_rows = target_s * threads / max(per_row, 1e-9)
+    oracle.decode_workload(w, seq_ids=[first], threads=1)
+    per_row = (time.perf_counter() - t0) / max(int(lengths[first]) * max(int(qo[first]), 1), 1)
+    budget_rows = target_s / max(per_row, 1e-9)  # per_row is one thread's time
     take, rows = [], 0
     for b in order:
-        if rows + lengths[b] > budget_rows and take:
+        if rows + lengths[b] * max(int(qo[b]), 1) > budget_rows and take:
             break
         take.append(int(b))
-        rows += int(lengths[b])
+        rows += int(lengths[b]) * max(int(qo[b]), 1)
+    kv_rows = int(lengths[take].sum())
     # when the whole workload is smaller than the budget, time repeated passes over it
     passes, dt = 0, 0.0
     while passes == 0 or dt * threads < target_s:
@@ -111,9 +137,12 @@ def cpu_baseline(w, kv_bytes_per_row: float, target_s: float) -> dict:
         oracle.decode_workload(w, seq_ids=take, threads=threads)
         dt += time.perf_counter() - t0
         passes += 1
-    return {"value": passes * rows * kv_bytes_per_row / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(take)} of {len(lengths)} sequences ({rows} KV rows) x {passes} pass(es), fp64 C, "
-                      f"{dt:.2f} s wall"}
+    res = {"value": round(passes * kv_rows * kv_bytes_per_row / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{len(take)} of {len(lengths)} sequences ({kv_rows} KV rows) x {passes} pass(es), fp64 C, "
+                     f"{dt:.2f} s wall on {threads} threads"}
+    res.update(_cpu_description())
+    return res
 
 
 def _source_sha256() -> str:
@@ -128,6 +157,36 @@ def _measured_traffic(name: str):
     if name != t["workload"] or not t["source_sha256"] or t["source_sha256"] != _source_sha256():
         return None
     return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
+
+
+def read_ceiling(seconds: float) -> float:
+    """GB/s of the plain read kernel (mla_debug_stream_read) over one 1 GiB
+    buffer: a few warm-up launches, then up to 200 timed launches (about
+    `seconds`) between two HIP events, with a synchronisation every 50."""
+    import torch
+    import mla_decode_split_amd as mla
+
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        mla.mla_debug_stream_read(buf, nbytes, sink, stream)
+    torch.cuda.synchronize()
+    reps = max(10, min(200, int(seconds * 6e12 / nbytes)))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(reps):
+        mla.mla_debug_stream_read(buf, nbytes, sink, stream)
+        if i % 50 == 49:
+            b.record(stream)
+            b.synchronize()
+    b.record(stream)
+    torch.cuda.synchronize()
+    rate = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return rate
 
 
 class Timed:
@@ -156,7 +215,7 @@ class Timed:
         t = time.perf_counter()
         self.plan = dev.plan_for(self.batch, rows_per_split=args.rows_per_split, wgs_per_cu=args.wgs_per_cu)
         self.t_plan = time.perf_counter() - t
-        self.ncopy = 1 if args.hot else max(1, min(8, math.ceil(768e6 / max(self.kv_bytes, 1))))
+        self.ncopy = 1 if args.hot else max(1, math.ceil(768e6 / max(self.kv_bytes, 1)))
         self.kvs = [self.batch.kv] + [self.batch.kv.clone() for _ in range(self.ncopy - 1)]
         self.out = torch.empty((self.batch.total_q, 16, 512), dtype=torch.bfloat16, device="cuda")
         self.ws = dev.workspace_for(self.plan)
@@ -199,26 +258,6 @@ class Timed:
         dev.run_merge(self.plan, self.batch, self.out, self.ws, self.stream)
         return 1e3 * a.elapsed_time(b) / steps
 
-    def read_ceiling(self, seconds=0.2):
-        """GB/s of the plain read kernel over the same rotated KV copies, over
-        about `seconds` of streaming (which also brings the device to its
-        working clocks before anything else is timed)."""
-        import torch
-        import mla_decode_split_amd as mla
-
-        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-        nbytes = self.kv_bytes // 16 * 16 if self.w.kv_dtype != "mxfp4" else self.kvs[0].numel() // 16 * 16
-        for i in range(3):
-            mla.mla_debug_stream_read(self.kvs[i % self.ncopy], nbytes, sink, self.stream)
-        reps = max(20, min(20000, int(seconds * 5e12 / max(nbytes, 1))))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(self.stream)
-        for i in range(reps):
-            mla.mla_debug_stream_read(self.kvs[i % self.ncopy], nbytes, sink, self.stream)
-        b.record(self.stream)
-        torch.cuda.synchronize()
-        return nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-
     def describe(self):
         import mla_decode_split_amd as mla
 
@@ -250,8 +289,8 @@ def main() -> int:
     threads = _host_threads()
     name = args.workload
 
+    ceiling = read_ceiling(args.read_ceiling_s) if args.read_ceiling_s > 0 else None
     h = Timed(name, args, threads, args.q_len)
-    ceiling = h.read_ceiling(args.read_ceiling_s) if args.read_ceiling_s > 0 else None
     # throughput: K whole calls back to back, nothing recorded between them
     elapsed = h.time(args.steps, args.warmup)
     # roofline: K stage-1 launches back to back between two events on their stream
@@ -302,19 +341,24 @@ def main() -> int:
         # the five workloads, and the headline shape with several query rows per sequence
         for other, q_len in [(n, 1) for n in synth.WORKLOADS] + [(DEFAULT_WORKLOAD, 2), (DEFAULT_WORKLOAD, 4)]:
             t = Timed(other, args, threads, q_len)
-            t.read_ceiling(0.05)
-            # about 50 ms of calls per workload, so that short calls are timed at
-            # the part's working clocks rather than across a host-side gap
+            # about 50 ms of calls per workload, after as many untimed, so that
+            # short calls are timed at the part's working clocks
             probe = t.time(20, args.warmup) / 20
             steps = int(min(20000, max(args.steps, 0.05 / max(probe, 1e-7))))
+            t.time(steps, 0)
             el = t.time(steps, 0)
             us = 1e6 * el / steps
+            s1 = t.split_launch_us(min(steps, 2000))
             d = t.describe()
-            table.append({"workload": t.name, "q_len": q_len, "us_per_call": round(us, 2), "calls": steps,
-                          "GBs": round(t.kv_bytes / (us * 1e-6) / 1e9, 1),
-                          "frac_of_peak": round(t.kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                          "kv_bytes": t.kv_bytes, "num_splits": d["num_splits"],
-                          "rows_per_split": d["rows_per_split"], "stage2": d["stage2"]})
+            row = {"workload": t.name, "q_len": q_len, "us_per_call": round(us, 2), "calls": steps,
+                   "GBs": round(t.kv_bytes / (us * 1e-6) / 1e9, 1),
+                   "frac_of_peak": round(t.kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "stage1_us": round(s1, 2), "stage1_frac_of_peak": round(t.kv_bytes / (s1 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "kv_bytes": t.kv_bytes, "kv_copies_rotated": t.ncopy, "num_splits": d["num_splits"],
+                   "rows_per_split": d["rows_per_split"], "stage2": d["stage2"]}
+            if not args.no_cpu_baseline and q_len == 1:
+                row["cpu_baseline"] = cpu_baseline(t.w, t.kv_bytes / t.rows, args.cpu_seconds)
+            table.append(row)
             del t
             torch.cuda.empty_cache()
         res["workloads"] = table
