@@ -342,6 +342,29 @@ __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+typedef const __attribute__((address_space(3))) uint8_t* lds_cbytes;
+
+// 16- and 8-byte loads through a global (flat) or an LDS pointer; the LDS
+// forms compile to ds_read, which the LDS counter tracks, not the memory one.
+__device__ inline u32x4 ld16(const uint8_t* p) { return *(const u32x4*)p; }
+__device__ inline u32x2 ld8(const uint8_t* p) { return *(const u32x2*)p; }
+__device__ inline u32x4 ld16(lds_cbytes p) { return *(const __attribute__((address_space(3))) u32x4*)p; }
+__device__ inline u32x2 ld8(lds_cbytes p) { return *(const __attribute__((address_space(3))) u32x2*)p; }
+typedef const __attribute__((address_space(3))) uint16_t* lds_chalves;
+__device__ inline u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
+__device__ inline u32x4 ld16(lds_chalves p) { return *(const __attribute__((address_space(3))) u32x4*)p; }
+// The 16-bit element pointer of the same address space as a byte pointer.
+template <typename BP>
+struct Elem16;
+template <>
+struct Elem16<const uint8_t*> {
+  using type = const uint16_t*;
+};
+template <>
+struct Elem16<lds_cbytes> {
+  using type = lds_chalves;
+};
+
 // 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane
 // (lds_base wave-uniform).  Issued through inline asm on purpose: the compiler
 // would otherwise treat every later LDS read as dependent on this write and
@@ -351,6 +374,13 @@ __device__ inline uint32_t lds_addr(const void* p) {
 __device__ inline void dma16(i32x4 r, uint32_t lds_base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
                : "memory", "m0");
+}
+
+// The same DMA without a memory clobber, for the loads a workgroup issues
+// before anything else (no LDS access precedes the wait that consumes them),
+// so that the scalar loads the compiler places after them stay scalar.
+__device__ inline void dma16_first(i32x4 r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r) : "m0");
 }
 
 // 4 bytes per active lane from rsrc + voff into LDS at lds_base + 4 * lane (the
@@ -662,8 +692,10 @@ struct QOperand {
   u32x4 rx;
   u32x2 r8[kBfChunks];
 
-  // Issues this wave's query loads (phase 1 of 3).
-  __device__ inline void fetch(const uint8_t* q, int64_t qrow, int lane, int w) {
+  // Issues this wave's query loads (phase 1 of 3), from global memory or (q an
+  // LDS pointer) from a copy of the query rows staged in LDS.
+  template <typename BP>
+  __device__ inline void fetch(BP q, int64_t qrow, int lane, int w) {
     const int h = lane & 15, g = lane >> 4;
     const int64_t base = (qrow * kHeads + h) * kQK;
     bx = lx = 0;
@@ -677,30 +709,30 @@ struct QOperand {
     const int m0 = kFp4K ? 128 * w + 16 * g : 128 * w + 32 * g;  // first 16 dims of this lane's B part
     const int m1 = kFp4K ? m0 + 64 : m0 + 16;                     // second 16
     if constexpr (kFp8Codes) {
-      b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(*(const u32x4*)(q + base + m0),
-                                                             *(const u32x4*)(q + base + m1), 0, 1, 2, 3, 4, 5, 6, 7));
+      b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(ld16(q + base + m0), ld16(q + base + m1), 0, 1, 2, 3, 4,
+                                                             5, 6, 7));
       if (w < 2) {
         if constexpr (kByteK)
-          bx = *(const uint64_t*)(q + base + 512 + 32 * w + 8 * g);
+          bx = __builtin_bit_cast(uint64_t, ld8(q + base + 512 + 32 * w + 8 * g));
         else
-          r8[0] = *(const u32x2*)(q + base + 512 + 32 * w + 8 * g);
+          r8[0] = ld8(q + base + 512 + 32 * w + 8 * g);
       }
     } else if constexpr (kHiLo) {
-      const uint16_t* qb = (const uint16_t*)q + base;
-      raw[0] = *(const u32x4*)(qb + m0);
-      raw[1] = *(const u32x4*)(qb + m0 + 8);
-      raw[2] = *(const u32x4*)(qb + m1);
-      raw[3] = *(const u32x4*)(qb + m1 + 8);
-      if (w < 2) rx = *(const u32x4*)(qb + 512 + 32 * w + 8 * g);
+      const typename Elem16<BP>::type qb = (typename Elem16<BP>::type)q + base;  // bf16 elements
+      raw[0] = ld16(qb + m0);
+      raw[1] = ld16(qb + m0 + 8);
+      raw[2] = ld16(qb + m1);
+      raw[3] = ld16(qb + m1 + 8);
+      if (w < 2) rx = ld16(qb + 512 + 32 * w + 8 * g);
     } else {
 #pragma unroll
       for (int k = 0; k < kBfChunks; ++k) {
         const int c = w + 4 * k;
         if (c < kQK / 32) {
           if constexpr (QF == DT_BF16)
-            b[k] = *(const bf16x8*)(q + 2 * (base + 32 * c + 8 * g));
+            b[k] = __builtin_bit_cast(bf16x8, ld16(q + 2 * (base + 32 * c + 8 * g)));
           else
-            r8[k] = *(const u32x2*)(q + base + 32 * c + 8 * g);
+            r8[k] = ld8(q + base + 32 * c + 8 * g);
         } else {
           b[k] = bf16x8{};
           r8[k] = u32x2{0u, 0u};
@@ -1130,7 +1162,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
                             uint8_t* dtab,
                             const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow0, int nq, int64_t r0,
                             int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows,
-                            PageSpan ps) {
+                            PageSpan ps, bool staged) {
   using G = Geom<KF>;
   using DM = Dma<KF, PAGED>;
   constexpr int NS = Ring<KF, QL, PAGED>::kStages;
@@ -1229,11 +1261,21 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   if (PAGED && wd == 3)
     for (int t = 0; t <= NS - 2 + kIdxLead; ++t) stage_idx(t);
 
+  const int my_chunks = DM::chunks_of_wave(wd);
   QOperand<QF, KF> qop[QW];
+  if (staged) {
+    // The kernel issued tile 0, then this sequence's query row (into slot NS - 1),
+    // then tiles 1 .. NS - 2: wait for the first two and read the query from LDS.
+    if (my_chunks > 0) wait_tiles_behind<DM::kMaxChunksPerWave>(my_chunks, NS - 2);
+    lds_barrier();
+    qop[0].fetch((lds_cbytes)(ring + (NS - 1) * Ring<KF, QL, PAGED>::kStageBytes), 0, lane, w);
+    qop[0].arrive();
+  } else {
 #pragma unroll
-  for (int t = 0; t < QW; ++t) qop[t].fetch(p.q, qrow0 + std::min(tb + t, nq - 1), lane, w);
+    for (int t = 0; t < QW; ++t) qop[t].fetch(p.q, qrow0 + std::min(tb + t, nq - 1), lane, w);
 #pragma unroll
-  for (int t = 0; t < QW; ++t) qop[t].arrive();
+    for (int t = 0; t < QW; ++t) qop[t].arrive();
+  }
   const int pro = std::min(NS - 1, ntiles);
   if constexpr (PAGED) {
     if (wd == 3) {
@@ -1242,7 +1284,8 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
     }
     lds_barrier();
   }
-  for (int t = 0; t < pro; ++t) issue_tile(t);
+  if (!staged)
+    for (int t = 0; t < pro; ++t) issue_tile(t);
   // per-token head maxima past the sequence counts at the start of xchg
 #pragma unroll
   for (int t = 0; t < QW; ++t) qop[t].prepare(xchg + 256 + 64 * (tb + t), w, lane);
@@ -1258,7 +1301,6 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
     for (int j = 0; j < 8; ++j) ws[t].acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int my_chunks = DM::chunks_of_wave(wd);
   // tile i is complete in LDS and every wave is done with tile i - 1
   auto advance = [&](int i) {
     if (my_chunks > 0) {
@@ -1396,10 +1438,29 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   }
 }
 
-template <int QF, int KF, int QL, bool CAP, bool PAGED>
+// Each workgroup's first piece, derived by the planner from the host kv_indptr
+// and passed with the kernel arguments (read with scalar loads), where the
+// kernel would otherwise search kv_indptr and load the sequence bounds before
+// its first KV load.  Entry g: the piece's rows (bits 0-15; 0 = the range holds
+// no rows of any sequence), its sequence (bits 16-29), whether the sequence
+// starts at the range's first row (bit 30) and whether it ends inside the
+// range (bit 31).  The piece always starts at the range's first row.  Used with
+// one query row per sequence and contiguous bf16 or fp8 KV, when the plan
+// knows the offsets, kv_indptr[0] = 0, G <= kSplitTable, batch <= 2^14 and
+// R < 2^16.
+constexpr int kSplitTable = 640;
+struct SplitTable {
+  static constexpr bool kHas = true;
+  uint32_t first[kSplitTable];
+};
+struct NoSplitTable {
+  static constexpr bool kHas = false;
+};
+
+template <int QF, int KF, int QL, bool CAP, bool PAGED, typename Tab>
 __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attribute__((amdgpu_waves_per_eu(
     Ring<KF, QL, PAGED>::kWgsPerCu * RowSplit<QL>::kGroups,
-    Ring<KF, QL, PAGED>::kWgsPerCu * RowSplit<QL>::kGroups))) void mla_split_kernel(SplitParams p) {
+    Ring<KF, QL, PAGED>::kWgsPerCu * RowSplit<QL>::kGroups))) void mla_split_kernel(SplitParams p, Tab tab) {
   using RG = Ring<KF, QL, PAGED>;
   constexpr int kThreads = Geom<KF>::kThreads * RowSplit<QL>::kGroups;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kLdsBytes];
@@ -1416,33 +1477,79 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
   const int64_t hi = std::min<int64_t>(lo + p.rows_per_wg, p.total_kv);
   if (lo >= hi) return;
 
-  // Sequences overlapping [lo, hi): b in [#{j>=1: indptr[j] <= lo}, #{j<bs: indptr[j] < hi}).
-  if (tid < 2) counts[tid] = 0;
-  if (KF == DT_MXFP4 && (kThreads == 256 || tid < 256)) e8m0_lut[tid] = e8m0_f32(tid);  // one code per thread
-  __syncthreads();
-  int c_first = 0, c_end = 0;
-  for (int j = tid; j <= p.batch; j += kThreads) {
-    const int64_t v = p.kv_indptr[j];
-    c_first += (j >= 1 && v <= lo);
-    c_end += (j < p.batch && v < hi);
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    c_first += __shfl_xor(c_first, off, 64);
-    c_end += __shfl_xor(c_end, off, 64);
-  }
-  if ((tid & 63) == 0) {
-    atomicAdd(&counts[0], c_first);
-    atomicAdd(&counts[1], c_end);
-  }
-  __syncthreads();
-  const int b_first = uniform(counts[0]);
-  const int b_end = uniform(counts[1]);
-
   float qs = 1.f, ks = 1.f;
   if (QF == DT_FP8) qs = *p.q_scale;
   if (KF == DT_FP8) ks = *(const float*)p.kv_scale;
   const float score_scale = p.sm_scale * qs * ks * kLog2e;
   const float out_scale = ks;
+
+  int b_first, b_end;
+  if constexpr (Tab::kHas) {
+    // Staged start: tile 0 of the first piece (which starts at lo) goes out at
+    // once, then - with the piece's sequence from the table - that sequence's
+    // query row into the ring's last slot, then tiles 1 .. NS - 2; the piece
+    // waits for tile 0 and the query only.
+    static_assert(!PAGED && QL == 1 && KF != DT_MXFP4, "staged start: one query row, contiguous bf16 / fp8 KV");
+    using G = Geom<KF>;
+    using DM = Dma<KF, PAGED>;
+    constexpr int NS = RG::kStages;
+    const int wd = uniform(tid >> 6), lane = tid & 63;
+    const i32x4 rk = make_rsrc(p.kv + lo * G::kRow,
+                               (uint32_t)std::min<uint64_t>((uint64_t)(p.total_kv - lo) * G::kRow, 0xFFFFF000ull));
+    auto issue = [&](int t) {
+#pragma unroll
+      for (int k = 0; k < DM::kMaxChunksPerWave; ++k) {
+        const int c = wd + DM::kWaves * k;
+        if (c >= G::kRowChunks) break;
+        dma16_first(rk, uniform(lds_addr(ring + (t % NS) * RG::kStageBytes + c * 1024)),
+                    (uint32_t)(t * G::kRowBytes) + dma_src_offset<KF>(64 * c + lane));
+      }
+    };
+    issue(0);
+    const uint32_t v = tab.first[gi];
+    const int n_first = (int)(v & 0xffffu);
+    const int b0 = (int)((v >> 16) & 0x3fffu);
+    if (n_first > 0) {
+      constexpr uint32_t kQBytes = kHeads * kQK * (QF == DT_BF16 ? 2 : 1);
+      const i32x4 rq = make_rsrc(p.q + (int64_t)b0 * kQBytes, kQBytes);
+      for (int c = wd; c < (int)(kQBytes / 1024); c += DM::kWaves)
+        dma16_first(rq, uniform(lds_addr(ring + (NS - 1) * RG::kStageBytes + c * 1024)), (uint32_t)(c * 1024 + 16 * lane));
+      for (int t = 1; t < NS - 1; ++t) issue(t);
+      const int64_t s0 = (v >> 30) & 1u ? lo : lo - 1;  // only "before lo" matters below lo
+      const int64_t e0 = (v >> 31) ? lo + n_first : hi + 1;
+      split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab,
+                                          (const __attribute__((address_space(3))) float*)e8m0_lut, b0, 1, lo, n_first,
+                                          piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, p.rows_per_wg,
+                                          PageSpan{lo, p.total_kv - lo, 0}, true);
+      lds_barrier();  // the next piece refills the ring
+    }
+    wait_vmcnt<0>();  // nothing staged is still landing in LDS (a piece shorter than the ring)
+    if (n_first == 0 || lo + n_first >= hi) return;
+    b_first = b0 + 1;
+    b_end = p.batch;  // pieces until one starts at or past hi
+  } else {
+    // Sequences overlapping [lo, hi): b in [#{j>=1: indptr[j] <= lo}, #{j<bs: indptr[j] < hi}).
+    if (tid < 2) counts[tid] = 0;
+    if (KF == DT_MXFP4 && (kThreads == 256 || tid < 256)) e8m0_lut[tid] = e8m0_f32(tid);  // one code per thread
+    __syncthreads();
+    int c_first = 0, c_end = 0;
+    for (int j = tid; j <= p.batch; j += kThreads) {
+      const int64_t v = p.kv_indptr[j];
+      c_first += (j >= 1 && v <= lo);
+      c_end += (j < p.batch && v < hi);
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      c_first += __shfl_xor(c_first, off, 64);
+      c_end += __shfl_xor(c_end, off, 64);
+    }
+    if ((tid & 63) == 0) {
+      atomicAdd(&counts[0], c_first);
+      atomicAdd(&counts[1], c_end);
+    }
+    __syncthreads();
+    b_first = uniform(counts[0]);
+    b_end = uniform(counts[1]);
+  }
 
   for (int b = b_first; b < b_end; ++b) {
     // the loads are independent; issue them together
@@ -1451,6 +1558,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
     if constexpr (QL > 1) qe_raw = p.qo_indptr[b + 1];
     const int64_t s = uniform(s_raw);
     const int64_t e = uniform(e_raw);
+    if (Tab::kHas && s >= hi) break;
     const int64_t qrow0 = std::min(std::max(uniform(q_raw), 0), p.total_q - 1);
     int nq = 1;
     if constexpr (QL > 1) {
@@ -1471,7 +1579,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       ps = PageSpan{ok ? pb : 0, ok ? pe - pb : 0, (int32_t)(r0 - s)};
     }
     split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
-                            r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg, ps);
+                            r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg, ps, false);
     lds_barrier();  // the next piece refills the ring
   }
 }
@@ -1671,6 +1779,8 @@ struct mla_plan {
   size_t lse_offset;
   bool has_table;  // merge ranges known at plan time (host kv_indptr, batch and G small enough)
   MergeTable table;
+  bool has_split_table;  // each workgroup's first piece known at plan time (staged start)
+  SplitTable split_table;
 };
 
 namespace {
@@ -1720,12 +1830,19 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 template <int QF, int KF, bool CAP, bool PAGED>
 void launch_split_v(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
   const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads * (pl->ql == 4 ? RowSplit<4>::kGroups : 1));
+  if constexpr (!PAGED && KF != DT_MXFP4) {
+    if (pl->ql == 1 && pl->has_split_table) {
+      hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, SplitTable>), grid, block, 0, st, sp,
+                         pl->split_table);
+      return;
+    }
+  }
   if (pl->ql == 1)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, NoSplitTable>), grid, block, 0, st, sp, NoSplitTable{});
   else if (pl->ql == 2)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2, CAP, PAGED>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2, CAP, PAGED, NoSplitTable>), grid, block, 0, st, sp, NoSplitTable{});
   else
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4, CAP, PAGED>), grid, block, 0, st, sp);
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4, CAP, PAGED, NoSplitTable>), grid, block, 0, st, sp, NoSplitTable{});
 }
 
 template <int QF, int KF, bool PAGED>
@@ -1848,6 +1965,25 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
     }
   }
   pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
+  // Staged start (one query row, contiguous bf16 / fp8 KV): each workgroup's
+  // first piece from the host offsets, found by the kernel's own counting rule.
+  pl->has_split_table = kv_indptr_host && ql == 1 && !pr->kv_paged && pr->kv_dtype != DT_MXFP4 &&
+                        kv_indptr_host[0] == 0 && G <= kSplitTable && pr->batch_size <= (1 << 14) && R < (1 << 16);
+  if (pl->has_split_table) {
+    const int32_t* ind = kv_indptr_host;
+    int b = 0;  // first sequence with ind[b + 1] > lo, advanced with lo
+    for (int64_t g = 0; g < G; ++g) {
+      const int64_t lo = g * R, hi = std::min(lo + R, total);
+      while (b < pr->batch_size && ind[b + 1] <= lo) ++b;
+      uint32_t v = 0;  // no rows of any sequence
+      if (b < pr->batch_size && lo < ind[pr->batch_size]) {
+        const int64_t s = ind[b], e = ind[b + 1];  // s <= lo < e
+        v = (uint32_t)(std::min(e, hi) - lo) | ((uint32_t)b << 16) | ((s == lo ? 1u : 0u) << 30) |
+            ((e <= hi ? 1u : 0u) << 31);
+      }
+      pl->split_table.first[g] = v;
+    }
+  }
   *plan_out = pl;
   if (workspace_bytes) *workspace_bytes = pl->ws_bytes;
   return MLA_OK;
