@@ -11,7 +11,9 @@ resident in the 256 MB last-level cache: the bandwidth is HBM bandwidth, not
 cache bandwidth.
 
 Prints one JSON line: value = KV bytes read per second over the timed steps
-(GB/s; K calls back to back between two synchronisations), plus per-call
+(GB/s; K calls back to back between two synchronisations, after W warm-up
+calls that follow about 0.1 s of untimed calls which settle the device's
+clocks to this kernel), plus per-call
 microseconds, the stage-1 kernel's roofline (its average launch duration from
 K stage-1 launches back to back between two HIP events on the launch stream)
 and the CPU oracle timed on a bounded sample of the same workload.  The table
@@ -69,12 +71,14 @@ def _args():
                     help="query rows per sequence (multi-token prediction / speculative decoding)")
     ap.add_argument("--rows-per-split", type=int, default=0)
     ap.add_argument("--wgs-per-cu", type=int, default=0)
+    ap.add_argument("--age-skew", type=int, default=0,
+                    help="per mille of the range moved to each CU's first workgroup (0 planner, -1 none)")
     ap.add_argument("--hot", action="store_true", help="no KV rotation (cache-resident numbers, secondary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU thread-seconds of each oracle sample")
     ap.add_argument("--only-headline", action="store_true", help="skip the per-workload table")
-    ap.add_argument("--read-ceiling-s", type=float, default=0.03,
+    ap.add_argument("--read-ceiling-s", type=float, default=0.2,
                     help="seconds of the plain read kernel over one 1 GiB buffer (at most 200 launches; 0: skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MB (reference for HBM counters)")
@@ -213,7 +217,8 @@ class Timed:
         self.rows = int(self.w.kv_indptr[-1] - self.w.kv_indptr[0])
         self.batch = dev.upload(self.w)
         t = time.perf_counter()
-        self.plan = dev.plan_for(self.batch, rows_per_split=args.rows_per_split, wgs_per_cu=args.wgs_per_cu)
+        self.plan = dev.plan_for(self.batch, rows_per_split=args.rows_per_split, wgs_per_cu=args.wgs_per_cu,
+                                 age_skew=getattr(args, "age_skew", 0))
         self.t_plan = time.perf_counter() - t
         self.ncopy = 1 if args.hot else max(1, math.ceil(768e6 / max(self.kv_bytes, 1)))
         self.kvs = [self.batch.kv] + [self.batch.kv.clone() for _ in range(self.ncopy - 1)]
@@ -227,6 +232,18 @@ class Timed:
 
         self.batch.kv = self.kvs[i % self.ncopy]
         dev.run(self.plan, self.batch, self.out, self.ws, self.stream)
+
+    def settle(self, seconds):
+        """Untimed calls for about `seconds` (device clocks settle to this kernel)."""
+        import torch
+
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                self.step(i)
+                i += 1
+            torch.cuda.synchronize()
 
     def time(self, steps, warmup):
         """Seconds for `steps` whole calls back to back, after `warmup` untimed ones."""
@@ -267,7 +284,8 @@ class Timed:
                 "page_size": int(getattr(self.w, "page_size", 1)),
                 "q_dtype": self.w.q_dtype, "kv_dtype": self.w.kv_dtype, "kv_rows": self.rows,
                 "kv_bytes": self.kv_bytes, "kv_copies_rotated": self.ncopy, "num_splits": d["num_splits"],
-                "rows_per_split": d["rows_per_split"], "stage2": bool(d["stage2"])}
+                "rows_per_split": d["rows_per_split"], "stage2": bool(d["stage2"]),
+                "paired_splits": d["paired_splits"], "second_rows_per_split": d["second_rows_per_split"]}
 
 
 def main() -> int:
@@ -289,8 +307,12 @@ def main() -> int:
     threads = _host_threads()
     name = args.workload
 
-    ceiling = read_ceiling(args.read_ceiling_s) if args.read_ceiling_s > 0 else None
     h = Timed(name, args, threads, args.q_len)
+    ceiling = read_ceiling(args.read_ceiling_s) if args.read_ceiling_s > 0 else None
+    # about 0.1 s of decode calls before the W warm-up steps: the device settles
+    # its clocks to the kernel it runs (after the read kernel or the host-side
+    # input generation, the first few ms of calls run up to 5 % slower)
+    h.settle(0.1)
     # throughput: K whole calls back to back, nothing recorded between them
     elapsed = h.time(args.steps, args.warmup)
     # roofline: K stage-1 launches back to back between two events on their stream
@@ -341,11 +363,11 @@ def main() -> int:
         # the five workloads, and the headline shape with several query rows per sequence
         for other, q_len in [(n, 1) for n in synth.WORKLOADS] + [(DEFAULT_WORKLOAD, 2), (DEFAULT_WORKLOAD, 4)]:
             t = Timed(other, args, threads, q_len)
-            # about 50 ms of calls per workload, after as many untimed, so that
+            # about 50 ms of calls per workload, after 0.1 s untimed, so that
             # short calls are timed at the part's working clocks
+            t.settle(0.1)
             probe = t.time(20, args.warmup) / 20
             steps = int(min(20000, max(args.steps, 0.05 / max(probe, 1e-7))))
-            t.time(steps, 0)
             el = t.time(steps, 0)
             us = 1e6 * el / steps
             s1 = t.split_launch_us(min(steps, 2000))

@@ -91,11 +91,19 @@ typedef struct mla_plan_options {
                              (default: as many as are resident together - with one query row
                              per sequence 2 for bf16 and fp8 KV, 3 for MXFP4 KV; see
                              mla_plan_desc.wgs_per_cu for others) */
+  int32_t age_skew;       /* with two stage-1 workgroups per CU (G = 2 * num_cus), per mille of
+                             R moved from each CU's second workgroup to its first (dispatched
+                             first, and favoured by the hardware), whose ranges are then
+                             adjacent (see mla_plan_desc.num_splits): 0 = planner's choice,
+                             -1 = equal ranges, 1..500 = that much */
 } mla_plan_options;
 
 /* What a plan decided (for tests, benchmarks and logs). */
 typedef struct mla_plan_desc {
-  int32_t num_splits;      /* stage-1 workgroups G; workgroup g owns KV rows [g*R, min((g+1)*R, total_kv)) */
+  int32_t num_splits;      /* stage-1 workgroups G.  F = paired_splits = 0: workgroup g owns KV rows
+                              [g*R, (g+1)*R).  F > 0 (then G = 2F): workgroups i and F + i - a
+                              CU's first and second - own the rows [i*P, i*P + R) and
+                              [i*P + R, (i+1)*P) with P = R + R2.  Ranges are clipped to total_kv */
   int32_t rows_per_split;  /* R, a multiple of tile_rows */
   int32_t tile_rows;       /* KV rows per LDS tile */
   int32_t stages;          /* depth of the LDS tile ring */
@@ -109,6 +117,8 @@ typedef struct mla_plan_desc {
   int32_t wgs_per_cu;      /* stage-1 workgroups per CU the plan is sized for (resident together) */
   int32_t query_tokens;    /* query rows of a sequence each stage-1 workgroup multiplies every KV
                               tile with: 1, 2 or 4 (max_q_len rounded up) */
+  int32_t paired_splits;   /* F: 0 for equal ranges, else the CU count (see num_splits) */
+  int32_t second_rows_per_split; /* R2 <= R, a multiple of tile_rows: rows of workgroups g >= F when paired */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan;

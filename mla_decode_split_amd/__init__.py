@@ -31,14 +31,15 @@ class mla_problem(ctypes.Structure):
 
 
 class mla_plan_options(ctypes.Structure):
-    _fields_ = [("rows_per_split", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32)]
+    _fields_ = [("rows_per_split", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32), ("age_skew", ctypes.c_int32)]
 
 
 class mla_plan_desc(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("rows_per_split", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("partial_slots", ctypes.c_int32), ("stage2", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("wgs_per_cu", ctypes.c_int32), ("query_tokens", ctypes.c_int32)]
+                ("wgs_per_cu", ctypes.c_int32), ("query_tokens", ctypes.c_int32),
+                ("paired_splits", ctypes.c_int32), ("second_rows_per_split", ctypes.c_int32)]
 
 
 class MlaError(RuntimeError):

@@ -213,16 +213,49 @@ struct Ring {
 // ------------------------------------------------------------ piece rules
 // Shared by the kernels and by the host replay used in tests.
 
+// The cut of the KV rows [0, total_kv) into workgroup ranges, in row order
+// ("positions").  Equal ranges (first = 0): position p is workgroup p and owns
+// ra rows.  Paired ranges (first = F, G = 2F): a CU's first workgroup, i < F
+// (dispatched before the rest), and its second, F + i, own the two halves of
+// pair i's 2R rows - ra rows then rb = 2R - ra - at positions 2i and 2i + 1.
+// The SIMD arbiter favours the older workgroup on a CU, so a slightly longer
+// range for it evens out their finish times, and pair boundaries stay where
+// equal ranges would put them.
+struct Cut {
+  int64_t ra, rb;
+  int32_t first, G;
+  __host__ __device__ int32_t pos_of(int32_t g) const {
+    return first ? (g < first ? 2 * g : 2 * (g - first) + 1) : g;
+  }
+  __host__ __device__ int32_t wg_at(int32_t pos) const { return first ? ((pos & 1) ? first + (pos >> 1) : pos >> 1) : pos; }
+  __host__ __device__ int64_t lo_at(int32_t pos) const {
+    return first ? (int64_t)(pos >> 1) * (ra + rb) + ((pos & 1) ? ra : 0) : (int64_t)pos * ra;
+  }
+  // position owning `row` (clamped to the last)
+  __host__ __device__ int32_t pos_of_row(int64_t row) const {
+    int64_t pos;
+    if (first) {
+      const int64_t i = row / (ra + rb);
+      pos = 2 * i + (row - i * (ra + rb) >= ra ? 1 : 0);
+    } else {
+      pos = row / ra;
+    }
+    return (int32_t)std::min<int64_t>(pos, G - 1);
+  }
+};
+
 // Slot of the piece of sequence [s, e) inside workgroup range [lo, hi):
 // -1 when the whole sequence is inside the range (written to out directly).
 __host__ __device__ inline int32_t piece_slot(int64_t s, int64_t e, int64_t lo, int64_t hi, int32_t g) {
   return (s >= lo && e <= hi) ? -1 : 2 * g + (s < lo ? 0 : 1);
 }
 
-// Stage-2 view of the same rule: sequence [s, e), e > s, touches workgroups
-// g0..g1; the piece in g0 starts inside that range (slot 2*g0 + 1), every
-// later piece starts before its range (slot 2*g).
-__host__ __device__ inline int32_t merge_slot(int32_t g, int32_t g0) { return 2 * g + (g == g0 ? 1 : 0); }
+// Stage-2 view of the same rule: sequence [s, e), e > s, touches the ranges at
+// positions p0..p1; the piece at p0 starts inside its range (slot 2g + 1 of
+// that range's workgroup g), every later piece starts before its range (slot 2g).
+__host__ __device__ inline int32_t merge_slot(const Cut& cut, int32_t pos, int32_t p0) {
+  return 2 * cut.wg_at(pos) + (pos == p0 ? 1 : 0);
+}
 
 // ---------------------------------------------------------------- helpers
 
@@ -632,7 +665,7 @@ struct SplitParams {
   int64_t total_kv;
   int32_t total_q;
   int32_t batch;
-  int32_t rows_per_wg;
+  Cut cut;
   float sm_scale;
   float logit_cap;  // > 0: scaled scores soft-capped as cap * tanh(s / cap)
   const int32_t* kv_indices;      // paged KV: row or page indices
@@ -1473,8 +1506,9 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
 
   const int tid = threadIdx.x;
   const int32_t gi = blockIdx.x;
-  const int64_t lo = (int64_t)gi * p.rows_per_wg;
-  const int64_t hi = std::min<int64_t>(lo + p.rows_per_wg, p.total_kv);
+  const int32_t pos = p.cut.pos_of(gi);
+  const int64_t lo = p.cut.lo_at(pos);
+  const int64_t hi = std::min<int64_t>(p.cut.lo_at(pos + 1), p.total_kv);
   if (lo >= hi) return;
 
   float qs = 1.f, ks = 1.f;
@@ -1519,7 +1553,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       const int64_t e0 = (v >> 31) ? lo + n_first : hi + 1;
       split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab,
                                           (const __attribute__((address_space(3))) float*)e8m0_lut, b0, 1, lo, n_first,
-                                          piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, p.rows_per_wg,
+                                          piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, (int32_t)(hi - lo),
                                           PageSpan{lo, p.total_kv - lo, 0}, true);
       lds_barrier();  // the next piece refills the ring
     }
@@ -1579,7 +1613,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       ps = PageSpan{ok ? pb : 0, ok ? pe - pb : 0, (int32_t)(r0 - s)};
     }
     split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
-                            r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, p.rows_per_wg, ps, false);
+                            r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, (int32_t)(hi - lo), ps, false);
     lds_barrier();  // the next piece refills the ring
   }
 }
@@ -1594,8 +1628,7 @@ struct MergeParams {
   uint16_t* out;
   int64_t total_kv;
   int32_t total_q;
-  int32_t rows_per_wg;
-  int32_t num_wgs;
+  Cut cut;
 };
 
 // One workgroup of two waves per (sequence, query token, pair of heads); wave w
@@ -1606,7 +1639,7 @@ struct MergeParams {
 // O at ((s * QL + t) * 16 + h) * 512, LSE at (s * QL + t) * 16 + h.
 constexpr int kMergeBatch = 8;
 
-// Workgroup range g0..g1 of every sequence, derived by the planner from the
+// Range positions g0..g1 of every sequence, derived by the planner from the
 // host kv_indptr and passed with the kernel arguments (read in parallel with
 // them, where the offsets would be one more dependent load); g1 < g0 marks a
 // sequence with no rows.  Used when the plan knows the offsets, the batch
@@ -1647,8 +1680,8 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
   } else {
     const int64_t s = std::max<int64_t>(p.kv_indptr[b], 0);
     const int64_t e = std::min<int64_t>(p.kv_indptr[b + 1], p.total_kv);
-    g0 = (int32_t)std::min<int64_t>(s / p.rows_per_wg, p.num_wgs - 1);
-    g1 = e > s ? (int32_t)std::min<int64_t>((e - 1) / p.rows_per_wg, p.num_wgs - 1) : g0 - 1;
+    g0 = p.cut.pos_of_row(s);
+    g1 = e > s ? p.cut.pos_of_row(e - 1) : g0 - 1;
   }
   if (g1 < g0) {  // no KV rows: the softmax is empty, the output is zero
     *(u32x4*)o = u32x4{0u, 0u, 0u, 0u};
@@ -1664,7 +1697,7 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     u32x4 u[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int64_t slot = (int64_t)merge_slot(std::min(base + k, g1), g0) * QL + tq;
+      const int64_t slot = (int64_t)merge_slot(p.cut, std::min(base + k, g1), g0) * QL + tq;
       lse[k] = p.part_lse[slot * kHeads + h];
       u[k] = *(const u32x4*)(p.part_o + (slot * kHeads + h) * kV + 8 * t);
     }
@@ -1767,7 +1800,7 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 struct mla_plan {
   mla_problem prob;
-  int32_t rows_per_wg;
+  Cut cut;  // workgroup ranges: G = cut.G workgroups
   int32_t num_wgs;
   int32_t stages;
   int32_t lds_bytes;
@@ -1814,6 +1847,10 @@ RingInfo ring_info_for(int kv_dtype, int ql, bool paged) {
   return ql == 1 ? ring_info_for<1>(kv_dtype, paged)
                  : ql == 2 ? ring_info_for<2>(kv_dtype, paged) : ring_info_for<4>(kv_dtype, paged);
 }
+
+// Per mille of R moved to the first workgroup on each CU when there are more
+// workgroups than CUs (see Cut).
+constexpr int kDefaultAgeSkew = 150;
 
 // Smallest row range worth a workgroup: below it the partial write-back and the
 // merge cost more than the extra parallelism gains.
@@ -1899,7 +1936,8 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
     return MLA_ERR_INVALID_ARG;
   if (pr->q_dtype != DT_BF16 && pr->q_dtype != DT_FP8) return MLA_ERR_UNSUPPORTED;
   if (pr->kv_dtype != DT_BF16 && pr->kv_dtype != DT_FP8 && pr->kv_dtype != DT_MXFP4) return MLA_ERR_UNSUPPORTED;
-  if (opt && (opt->rows_per_split < 0 || opt->wgs_per_cu < 0)) return MLA_ERR_INVALID_ARG;
+  if (opt && (opt->rows_per_split < 0 || opt->wgs_per_cu < 0 || opt->age_skew < -1 || opt->age_skew > 500))
+    return MLA_ERR_INVALID_ARG;
 
   int num_cus = pr->num_cus;
   if (num_cus <= 0) {
@@ -1928,13 +1966,23 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   R = (R + kTile - 1) / kTile * kTile;
   R = std::min<int64_t>(R, (int64_t)1 << 20);  // keeps per-workgroup byte offsets in 32 bits
   const int64_t G = std::max<int64_t>((total + R - 1) / R, 1);
+  // With more workgroups than CUs, the first one on each CU (the first num_cus
+  // dispatched) takes `skew` per mille of R more rows and the later ones fewer,
+  // in whole tiles, so that the later ones - which the SIMD arbiter serves
+  // second - finish with it.
+  Cut cut{R, R, 0, (int32_t)G};
+  const int skew = opt && opt->age_skew != 0 ? opt->age_skew : kDefaultAgeSkew;
+  if (skew > 0 && G == 2 * (int64_t)num_cus) {
+    const int64_t d = (R * skew / 1000 + kTile / 2) / kTile * kTile;
+    if (d > 0 && d < R) cut = Cut{R + d, R - d, num_cus, (int32_t)G};
+  }
 
   bool stage2 = true;
   if (kv_indptr_host) {
     stage2 = false;
     for (int b = 0; b < pr->batch_size && !stage2; ++b) {
       const int64_t s = kv_indptr_host[b], e = kv_indptr_host[b + 1];
-      if (e <= s || s / R != (e - 1) / R) stage2 = true;
+      if (e <= s || cut.pos_of_row(s) != cut.pos_of_row(e - 1)) stage2 = true;
     }
   }
 
@@ -1942,7 +1990,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   if (!pl) return MLA_ERR_INVALID_ARG;
   pl->prob = *pr;
   pl->prob.num_cus = num_cus;
-  pl->rows_per_wg = (int32_t)R;
+  pl->cut = cut;
   pl->num_wgs = (int32_t)G;
   pl->stages = ri.stages;
   pl->lds_bytes = ri.lds_bytes;
@@ -1958,8 +2006,8 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
     for (int b = 0; b < pr->batch_size; ++b) {
       const int64_t s = std::max<int64_t>(kv_indptr_host[b], 0);
       const int64_t e = std::min<int64_t>(kv_indptr_host[b + 1], total);
-      const int64_t g0 = std::min<int64_t>(s / R, G - 1);
-      const int64_t g1 = e > s ? std::min<int64_t>((e - 1) / R, G - 1) : g0 - 1;
+      const int64_t g0 = cut.pos_of_row(s);
+      const int64_t g1 = e > s ? cut.pos_of_row(e - 1) : g0 - 1;
       // empty: g0 = 1 > g1 = 0
       pl->table.g01[b] = g1 < g0 ? 1u : (uint32_t)g0 | ((uint32_t)g1 << 16);
     }
@@ -1968,13 +2016,17 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   // Staged start (one query row, contiguous bf16 / fp8 KV): each workgroup's
   // first piece from the host offsets, found by the kernel's own counting rule.
   pl->has_split_table = kv_indptr_host && ql == 1 && !pr->kv_paged && pr->kv_dtype != DT_MXFP4 &&
-                        kv_indptr_host[0] == 0 && G <= kSplitTable && pr->batch_size <= (1 << 14) && R < (1 << 16);
+                        kv_indptr_host[0] == 0 && G <= kSplitTable && pr->batch_size <= (1 << 14) && cut.ra < (1 << 16);
   if (pl->has_split_table) {
     const int32_t* ind = kv_indptr_host;
-    int b = 0;  // first sequence with ind[b + 1] > lo, advanced with lo
     for (int64_t g = 0; g < G; ++g) {
-      const int64_t lo = g * R, hi = std::min(lo + R, total);
-      while (b < pr->batch_size && ind[b + 1] <= lo) ++b;
+      const int32_t pos = cut.pos_of((int32_t)g);
+      const int64_t lo = cut.lo_at(pos), hi = std::min(cut.lo_at(pos + 1), total);
+      int b = 0;  // first sequence with ind[b + 1] > lo
+      for (int lo_b = 0, hi_b = pr->batch_size; lo_b < hi_b;) {
+        const int mid = (lo_b + hi_b) / 2;
+        if (ind[mid + 1] <= lo) lo_b = b = mid + 1; else hi_b = mid;
+      }
       uint32_t v = 0;  // no rows of any sequence
       if (b < pr->batch_size && lo < ind[pr->batch_size]) {
         const int64_t s = ind[b], e = ind[b + 1];  // s <= lo < e
@@ -1994,7 +2046,9 @@ void mla_decode_plan_destroy(mla_plan* plan) { delete plan; }
 mla_status mla_decode_plan_describe(const mla_plan* pl, mla_plan_desc* d) {
   if (!pl || !d) return MLA_ERR_INVALID_ARG;
   d->num_splits = pl->num_wgs;
-  d->rows_per_split = pl->rows_per_wg;
+  d->rows_per_split = (int32_t)pl->cut.ra;
+  d->paired_splits = pl->cut.first;
+  d->second_rows_per_split = (int32_t)pl->cut.rb;
   d->tile_rows = kTile;
   d->stages = pl->stages;
   d->partial_slots = 2 * pl->num_wgs;
@@ -2010,10 +2064,11 @@ mla_status mla_decode_plan_describe(const mla_plan* pl, mla_plan_desc* d) {
 mla_status mla_decode_plan_pieces(const mla_plan* pl, const int32_t* ind, int64_t* rec, int64_t cap, int64_t* count) {
   if (!pl || !ind || !count || cap < 0 || (cap > 0 && !rec)) return MLA_ERR_INVALID_ARG;
   const int bs = pl->prob.batch_size;
-  const int64_t R = pl->rows_per_wg, total = pl->prob.total_kv;
+  const int64_t total = pl->prob.total_kv;
   int64_t n = 0;
   for (int32_t g = 0; g < pl->num_wgs; ++g) {
-    const int64_t lo = (int64_t)g * R, hi = std::min(lo + R, total);
+    const int32_t pos = pl->cut.pos_of(g);
+    const int64_t lo = pl->cut.lo_at(pos), hi = std::min(pl->cut.lo_at(pos + 1), total);
     if (lo >= hi) continue;
     int b_first = 0, b_end = 0;  // the counting rule the kernel applies
     for (int j = 0; j <= bs; ++j) {
@@ -2046,12 +2101,12 @@ mla_status mla_decode_plan_merge_slots(const mla_plan* pl, const int32_t* ind, i
   const int64_t s = std::max<int64_t>(ind[b], 0), e = std::min<int64_t>(ind[b + 1], pl->prob.total_kv);
   *count = 0;
   if (e <= s) return MLA_OK;
-  const int32_t g0 = (int32_t)std::min<int64_t>(s / pl->rows_per_wg, pl->num_wgs - 1);
-  const int32_t g1 = (int32_t)std::min<int64_t>((e - 1) / pl->rows_per_wg, pl->num_wgs - 1);
+  const int32_t g0 = pl->cut.pos_of_row(s);
+  const int32_t g1 = pl->cut.pos_of_row(e - 1);
   if (g0 == g1) return MLA_OK;
   int32_t n = 0;
-  for (int32_t g = g0; g <= g1; ++g, ++n)
-    if (n < cap) slots[n] = merge_slot(g, g0);
+  for (int32_t pos = g0; pos <= g1; ++pos, ++n)
+    if (n < cap) slots[n] = merge_slot(pl->cut, pos, g0);
   *count = n;
   return MLA_OK;
 }
@@ -2094,7 +2149,7 @@ mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, cons
   sp->total_kv = pr.total_kv;
   sp->total_q = pr.total_q;
   sp->batch = pr.batch_size;
-  sp->rows_per_wg = pl->rows_per_wg;
+  sp->cut = pl->cut;
   sp->sm_scale = pr.sm_scale;
   sp->logit_cap = pr.logit_cap;
   sp->kv_indices = kv_indices;
@@ -2108,8 +2163,7 @@ mla_status prepare(const mla_plan* pl, const void* q, const float* q_scale, cons
   mp->out = sp->out;
   mp->total_kv = pr.total_kv;
   mp->total_q = pr.total_q;
-  mp->rows_per_wg = pl->rows_per_wg;
-  mp->num_wgs = pl->num_wgs;
+  mp->cut = pl->cut;
   return MLA_OK;
 }
 
@@ -2215,8 +2269,7 @@ mla_status mla_decode_merge(const mla_plan* pl, const int32_t* qo_indptr, const 
   mp.out = (uint16_t*)out;
   mp.total_kv = pl->prob.total_kv;
   mp.total_q = pl->prob.total_q;
-  mp.rows_per_wg = pl->rows_per_wg;
-  mp.num_wgs = pl->num_wgs;
+  mp.cut = pl->cut;
   return launch_merge_stage(pl, mp, (hipStream_t)stream);
 }
 

@@ -58,7 +58,8 @@ def test_plans_for_the_five_workloads(name):
     ind = _indptr(lengths)
     plan = _plan(len(lengths), int(ind[-1]), spec["kv_dtype"], spec["q_dtype"], ind)
     d = mla.mla_decode_plan_describe(plan)
-    assert d["num_splits"] * d["rows_per_split"] >= ind[-1] > (d["num_splits"] - 1) * d["rows_per_split"]
+    lo_last, _ = _range(d, d["num_splits"] - 1)
+    assert _range(d, d["num_splits"] - 1)[1] >= ind[-1] > lo_last
     assert d["rows_per_split"] % d["tile_rows"] == 0
     assert d["partial_slots"] == 2 * d["num_splits"]
     assert d["lds_bytes"] * d["wgs_per_cu"] <= 160 * 1024  # that many workgroups fit a CU's LDS
@@ -67,17 +68,33 @@ def test_plans_for_the_five_workloads(name):
     _check_cut(plan, ind)
 
 
+def _range(d, g):
+    """Rows [lo, hi) of workgroup g as the plan description states its cut."""
+    R, R2, F = d["rows_per_split"], d["second_rows_per_split"], d["paired_splits"]
+    if F == 0:
+        return g * R, (g + 1) * R
+    assert d["num_splits"] == 2 * F and R2 % d["tile_rows"] == 0 and 0 < R2 < R
+    i = g if g < F else g - F
+    lo = i * (R + R2) + (0 if g < F else R)
+    return lo, lo + (R if g < F else R2)
+
+
 def _check_cut(plan, ind):
     d = mla.mla_decode_plan_describe(plan)
     rec = mla.mla_decode_plan_pieces(plan, ind)
     bs = len(ind) - 1
-    R, G = d["rows_per_split"], d["num_splits"]
+    G = d["num_splits"]
+    # the ranges tile the rows in order, each workgroup once
+    bounds = sorted(_range(d, g) for g in range(G))
+    assert bounds[0][0] == 0 and all(a[1] == b_[0] for a, b_ in zip(bounds, bounds[1:]))
+    assert bounds[-1][1] >= ind[-1]
     covered = np.zeros(int(ind[-1]), dtype=np.int32)
     slots_of = {b: [] for b in range(bs)}
     used = set()
     for g, b, r0, r1, slot in rec:
+        lo, hi = _range(d, g)
         assert ind[b] <= r0 < r1 <= ind[b + 1]
-        assert g * R <= r0 and r1 <= min((g + 1) * R, ind[-1])
+        assert lo <= r0 and r1 <= min(hi, ind[-1])
         covered[r0:r1] += 1
         if slot >= 0:
             assert slot < d["partial_slots"] and slot // 2 == g
@@ -295,3 +312,31 @@ def test_paged_argument_errors_before_any_launch():
 
 def test_plan_destroy_accepts_null():
     mla.library().mla_decode_plan_destroy(None)
+
+
+@pytest.mark.parametrize("skew", [0, -1, 25, 120, 500])
+@pytest.mark.parametrize("lengths,rows,cus", [
+    ([512] * 8, 256, 8),                       # uniform: pair boundaries on sequence boundaries
+    ([4096] * 64, 1024, 128),                  # the bs64 x 4096 shape on 128 CUs
+    ([700, 1000, 33, 1, 2500, 77, 300], 160, 0),
+    ([700, 1000, 33, 1, 2500, 77, 300, 189], 150, 15),  # ragged, 30 ranges on 15 CUs
+    ([1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129], 0, 4),
+])
+def test_paired_cut(lengths, rows, cus, skew):
+    """With two workgroups per CU the first on each CU takes a longer range and
+    the second the rest of their pair's rows; every KV row is still covered
+    once and stage 2 merges exactly the partial pieces."""
+    ind = _indptr(lengths)
+    total = int(ind[-1])
+    if cus == 0:  # as many CUs as make two workgroups each
+        cus = ((total + rows - 1) // rows) // 2
+    prob = mla.make_problem(len(lengths), total, "bf16", "fp8", num_cus=cus)
+    opts = mla.mla_plan_options(rows, 0, skew)
+    plan = mla.mla_decode_plan(prob, opts, ind)
+    d = mla.mla_decode_plan_describe(plan)
+    paired = d["num_splits"] == 2 * cus and skew != -1 and d["paired_splits"] > 0
+    if skew == -1 or d["num_splits"] != 2 * cus:
+        assert d["paired_splits"] == 0
+    elif paired:
+        assert d["paired_splits"] == cus and d["second_rows_per_split"] < d["rows_per_split"]
+    _check_cut(plan, ind)

@@ -309,8 +309,12 @@ def _paged_equals_contiguous(w, pw, rows_per_split=0, what=""):
     the outputs agree bit for bit."""
     b, pb = dev.upload(w), dev.upload(pw)
     paged_plan = dev.plan_for(pb, rows_per_split=rows_per_split)
-    rows = mla.mla_decode_plan_describe(paged_plan)["rows_per_split"]
-    o1 = dev.run(dev.plan_for(b, rows_per_split=rows), b)
+    d = mla.mla_decode_plan_describe(paged_plan)
+    # the same cut: the base range length (paired ranges split 2R unevenly)
+    rows = (d["rows_per_split"] + d["second_rows_per_split"]) // 2 if d["paired_splits"] else d["rows_per_split"]
+    plan = dev.plan_for(b, rows_per_split=rows)
+    assert mla.mla_decode_plan_describe(plan)["num_splits"] == d["num_splits"]
+    o1 = dev.run(plan, b)
     o2 = dev.run(paged_plan, pb)
     torch.cuda.synchronize()
     same = bool(torch.equal(o1.view(torch.int16), o2.view(torch.int16)))
@@ -556,3 +560,26 @@ def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     ref, _ = oracle.decode_workload(w, threads=_host_threads())
     _compare(_bf16_out_to_f64(o1), ref, f"staged start {q_dtype}/{kv_dtype} rows {rows}")
+
+
+# ------------------------------------------------------------- paired ranges
+
+@pytest.mark.parametrize("skew", [120, 250])
+@pytest.mark.parametrize("kv_dtype,q_len,paged", [("fp8", 1, False), ("bf16", 1, False), ("mxfp4", 1, False),
+                                                  ("fp8", 2, False), ("fp8", 1, True), ("mxfp4", 2, True)])
+def test_paired_ranges(kv_dtype, q_len, paged, skew):
+    """Plans whose CUs each take a longer first and a shorter second range
+    (planned here for 15 CUs, so 30 ranges over a ragged batch, pieces crossing
+    pair boundaries) against the oracle, in every stage-1 variant family."""
+    lengths = [700, 1000, 33, 1, 2500, 77, 300, 189]
+    w = synth.make_batch(lengths, "bf16", kv_dtype, seed=1212 + skew, name="paired", q_lens=[q_len] * len(lengths))
+    if paged:
+        w = synth.page_workload(w, seed=1213, spare_rows=200)
+    b = dev.upload(w)
+    plan = dev.plan_for(b, rows_per_split=150, num_cus=15, age_skew=skew)
+    d = mla.mla_decode_plan_describe(plan)
+    assert d["paired_splits"] == 15 and d["num_splits"] == 30
+    out = dev.run(plan, b, workspace=dev.workspace_for(plan, fill=float("nan")))
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_workload(w, threads=_host_threads())
+    _compare(_bf16_out_to_f64(out), ref, f"paired ranges kv={kv_dtype} q_len={q_len} paged={paged} skew={skew}")
