@@ -200,10 +200,9 @@ struct Ring {
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static constexpr int kXchg = QL * kXchgBytes;
   static constexpr int kPBuf = 2 * (QL - 1) * kPTokBytes;
-  static constexpr int kLut = KF == DT_MXFP4 ? 1024 : 0;  // E8M0 code -> fp32 table
   static constexpr int kIdx = PAGED ? kIdxSlots * kTile * 4 : 0;
   static constexpr int kDtab = PAGED && KF == DT_MXFP4 ? kStages * kTile : 0;  // scale window offsets
-  static constexpr int kTotal = kLdsBytes + kXchg + kPBuf + kLut + kIdx + kDtab;
+  static constexpr int kTotal = kLdsBytes + kXchg + kPBuf + kIdx + kDtab;
   static_assert(kWgsPerCu * kTotal <= 160 * 1024, "resident workgroups per CU must fit the LDS");
   static_assert((kStages - 2) * Dma<KF, PAGED>::kMaxChunksPerWave <= 63, "vmcnt range");
   static_assert(kStages >= 2 && kStages - 3 <= 5, "tiles behind the one needed near the end: 0..5");
@@ -275,11 +274,13 @@ __device__ inline bf16x8 fp8x8_bf16(u32x2 v) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// E8M0 scale byte -> fp32 2^(e-127) (e = 0 is the fp32 subnormal 2^-127, 255 is NaN).
-__device__ inline float e8m0_f32(uint32_t e) {
-  const uint32_t b = e == 255u ? 0x7fc00000u : (e ? (e << 23) : 0x00400000u);
-  return __builtin_bit_cast(float, b);
-}
+// E8M0 scale byte e -> the fp32 scale operand of the scaled conversions below.
+// Those instructions take only the exponent field of their fp32 scale, so the
+// float whose exponent field is e scales by 2^(e-127) for every code - e = 0
+// (2^-127) and e = 255 (NaN) included: on gfx950 it gives the same bits as the
+// fp32 values 2^-127 and NaN for every pair of E2M1 codes (checked over all
+// 256 x 256 cases).  One shift, where a table would cost an LDS read.
+__device__ inline float e8m0_scale(uint32_t e) { return __builtin_bit_cast(float, e << 23); }
 
 // Byte SEL of w holds two E2M1 codes (low nibble = lower element) -> two bf16 times scale.
 template <int SEL>
@@ -492,8 +493,6 @@ struct LaneOffs {
   int xw[2][2];
   int kr[2];
   int kb[2];
-  // E2M1 keys: E8M0 code -> fp32 scale (e8m0_f32 of every code, in LDS)
-  const __attribute__((address_space(3))) float* e8m0;
 
   __device__ inline void init(int m, int g, int w) {
     constexpr int R = Geom<KF>::kRow;
@@ -632,7 +631,7 @@ __device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q,
       } else {
         const uint32_t w = *(const uint32_t*)(st + lo.v[(i & 3) >> 1] + pv_row_base(i) * R + 64 * q);
         const uint32_t e = st[sc.at(4 * g, pv_row_base(i)) + 4 * q + (m >> 2)];
-        x[i] = __builtin_bit_cast(u32x4, fp4x8_bf16(w, lo.e8m0[e]));
+        x[i] = __builtin_bit_cast(u32x4, fp4x8_bf16(w, e8m0_scale(e)));
       }
       if (MASK && pv_row(g, i) >= valid) x[i] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -935,7 +934,7 @@ __device__ inline void qk_tile(const uint8_t* st, const QOperand<QF, KF> (&qo)[Q
         // rope dims 512 + 32w + 8g + [0, 8), widened to bf16 with their block scale
         const uint32_t word = *(const uint32_t*)(st + lo.kr[blk]);
         const uint32_t e = st[sc.at(m, 16 * blk) + 16 + w];
-        const bf16x8 kb = fp4x8_bf16(word, lo.e8m0[e]);
+        const bf16x8 kb = fp4x8_bf16(word, e8m0_scale(e));
 #pragma unroll
         for (int t = 0; t < QL; ++t)
           s[t][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qo[t].br, s[t][blk], 0, 0, 0);
@@ -1193,7 +1192,7 @@ __device__ inline void set_priority(int prio) {
 template <int QF, int KF, int QL, bool CAP, bool PAGED>
 __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf, int32_t* idxring,
                             uint8_t* dtab,
-                            const __attribute__((address_space(3))) float* e8m0_lut, int64_t qrow0, int nq, int64_t r0,
+                            int64_t qrow0, int nq, int64_t r0,
                             int n, int32_t slot, float score_scale, float out_scale, int64_t wg_hi, int32_t wg_rows,
                             PageSpan ps, bool staged) {
   using G = Geom<KF>;
@@ -1271,7 +1270,6 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
 
   LaneOffs<KF> lo;
   lo.init(m, g, w);
-  lo.e8m0 = e8m0_lut;
 
   // Paged KV: wave 3 stages the physical row indices of tile t (32 lanes, 4
   // bytes each) into index slot t % kIdxSlots, kIdxLead tiles ahead of the
@@ -1499,7 +1497,6 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kLdsBytes];
   __shared__ float xchg[RG::kXchg / 4];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[QL > 1 ? RG::kPBuf : 16];
-  __shared__ float e8m0_lut[KF == DT_MXFP4 ? 256 : 1];
   __shared__ __attribute__((aligned(16))) int32_t idxring[PAGED ? kIdxSlots * kTile : 1];
   __shared__ __attribute__((aligned(16))) uint8_t dtab[RG::kDtab ? RG::kDtab : 1];
   int* counts = (int*)xchg;  // the sequence search runs before any exchange
@@ -1552,7 +1549,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       const int64_t s0 = (v >> 30) & 1u ? lo : lo - 1;  // only "before lo" matters below lo
       const int64_t e0 = (v >> 31) ? lo + n_first : hi + 1;
       split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab,
-                                          (const __attribute__((address_space(3))) float*)e8m0_lut, b0, 1, lo, n_first,
+                                          b0, 1, lo, n_first,
                                           piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, (int32_t)(hi - lo),
                                           PageSpan{lo, p.total_kv - lo, 0}, true);
       lds_barrier();  // the next piece refills the ring
@@ -1564,7 +1561,6 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
   } else {
     // Sequences overlapping [lo, hi): b in [#{j>=1: indptr[j] <= lo}, #{j<bs: indptr[j] < hi}).
     if (tid < 2) counts[tid] = 0;
-    if (KF == DT_MXFP4 && (kThreads == 256 || tid < 256)) e8m0_lut[tid] = e8m0_f32(tid);  // one code per thread
     __syncthreads();
     int c_first = 0, c_end = 0;
     for (int j = tid; j <= p.batch; j += kThreads) {
@@ -1612,7 +1608,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       const bool ok = pb >= 0 && pe >= pb;
       ps = PageSpan{ok ? pb : 0, ok ? pe - pb : 0, (int32_t)(r0 - s)};
     }
-    split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab, (const __attribute__((address_space(3))) float*)e8m0_lut, qrow0, nq,
+    split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab, qrow0, nq,
                             r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, (int32_t)(hi - lo), ps, false);
     lds_barrier();  // the next piece refills the ring
   }
@@ -1756,7 +1752,7 @@ __global__ void mla_debug_decode_kernel(int kv_dtype, const uint8_t* codes, cons
     const int64_t row = i / 72;
     const int c0 = 8 * (int)(i % 72);
     const uint32_t w = *(const uint32_t*)(codes + row * 288 + c0 / 2);
-    const bf16x8 d = fp4x8_bf16(w, e8m0_f32(scales[row * kScaleRow + c0 / 32]));
+    const bf16x8 d = fp4x8_bf16(w, e8m0_scale(scales[row * kScaleRow + c0 / 32]));
     for (int k = 0; k < 8; ++k) out[row * kQK + c0 + k] = (float)d[k];
   } else {
     if (i >= n) return;
