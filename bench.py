@@ -48,9 +48,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "f49d9a821f17bb05dc53cf4b6b9bd48951301f56be0c367faa023478db8eb872",
-    "fetch_kib": 152171.7,
-    "write_kib": 8224.0,
+    "source_sha256": "8ba04461e91546e6d600244de3f950d0fd96a7d7312ef448ceba34937573e56e",
+    "fetch_kib": 149904.6,
+    "write_kib": 8226.7,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
