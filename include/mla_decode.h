@@ -124,7 +124,15 @@ typedef struct mla_plan_desc {
 typedef struct mla_plan mla_plan;
 
 /*
- * Plan a decode.  Host-only: no device memory is touched and no HIP call is
+ * Plan a decode: how many stage-1 workgroups, and which KV rows each takes.
+ * This is the split-count choice of page kernelbot-amd-mixed-mla-586148 (its
+ * docstring's "Adaptive num_splits" and the host code that aims at a fixed
+ * number of programs for the GPU) and of page kernelbot-amd-mixed-mla-753817
+ * ("Entry point": the split count picked from batch size and KV length before
+ * stage 1 launches).  Here the rows of the whole batch are cut into ranges
+ * sized to the CU count, so that one sequence may span several ranges and one
+ * range several sequences.
+ * Host-only: no device memory is touched and no HIP call is
  * made unless problem->num_cus == 0.
  *   problem         shape and dtypes (see mla_problem).
  *   options         NULL or overrides.
@@ -145,7 +153,12 @@ mla_status mla_decode_plan(const mla_problem* problem, const mla_plan_options* o
 
 /*
  * Run a planned decode asynchronously on `stream` (stage 1, then stage 2 when
- * the plan needs it).  No allocation, no host<->device copy, no synchronisation.
+ * the plan needs it): the custom_kernel call of page kernelbot-amd-mixed-mla-753817
+ * ("Entry point": stage 1 over the splits, stage 2 only when a sequence has
+ * more than one), computing the output the template page
+ * kernelbot-amd-mixed-mla-675627 defines ("Input tuple", "Output";
+ * custom_kernel_bf16 is its plain form).  The argument shapes below are that
+ * input tuple's.  No allocation, no host<->device copy, no synchronisation.
  * All device pointers must be 16-byte aligned.
  *   q          device, [total_q][16][576]: bf16, or fp8 E4M3FN codes when q_dtype is fp8.
  *   q_scale    device fp32[1] (fp8 q: q = code * q_scale, q_scale >= 0); ignored for bf16 q (may be NULL).
@@ -249,7 +262,9 @@ mla_status mla_decode_plan_describe(const mla_plan* plan, mla_plan_desc* desc);
 
 /*
  * Host replay of how stage 1 cuts the batch (the same piece rule the kernel
- * uses), for tests and tooling.  Writes up to `capacity` records of 5 int64
+ * uses), for tests and tooling: which KV rows of which sequence each program
+ * takes (page kernelbot-amd-mixed-mla-586148, docstring: each program takes
+ * its share of the KV tokens and writes a partial).  Writes up to `capacity` records of 5 int64
  * each: {workgroup g, sequence b, first row, end row, slot (-1 = written to out
  * directly)} in workgroup order, and the total number of records to *count.
  * kv_indptr_host as in mla_decode_plan (required here).
@@ -259,7 +274,8 @@ mla_status mla_decode_plan_pieces(const mla_plan* plan, const int32_t* kv_indptr
 
 /*
  * Partial slots stage 2 merges for sequence b (host replay of the stage-2
- * rule).  Writes up to `capacity` slot indices to `slots` and the number of
+ * rule; page kernelbot-amd-mixed-mla-753817, "Stage 2: LSE-weighted
+ * reduction of split partial outputs").  Writes up to `capacity` slot indices to `slots` and the number of
  * slots to *count (0 when the sequence was written directly or is empty).
  */
 mla_status mla_decode_plan_merge_slots(const mla_plan* plan, const int32_t* kv_indptr_host, int32_t b,
@@ -267,7 +283,10 @@ mla_status mla_decode_plan_merge_slots(const mla_plan* plan, const int32_t* kv_i
 
 /*
  * Decode stored KV codes to fp32 with the device functions the decode kernel
- * uses (for bit-exactness tests of the dequantisation).
+ * uses (for bit-exactness tests of the dequantisation).  The formats are the
+ * template page's (kernelbot-amd-mixed-mla-675627, "Input tuple": fp8 codes
+ * with one scalar scale, fp4x2 bytes with fp8_e8m0 scales), read as the OCP
+ * fp8 and MX definitions give them.
  *   MLA_DTYPE_FP8_E4M3FN: codes = n bytes, scales = device fp32[1] or NULL (1.0);
  *                         out[i] = fp32(value(code_i)) * scale, one fp32 rounding.
  *   MLA_DTYPE_MXFP4:      codes = n rows of 288 bytes, scales = n rows of 18 bytes;
@@ -280,7 +299,8 @@ mla_status mla_debug_decode(int32_t kv_dtype, const void* codes, const void* sca
                             void* stream);
 
 /*
- * Read-bandwidth reference for reports (not part of the decode): one launch
+ * Read-bandwidth reference for reports (not part of the decode, and defined by
+ * none of the pages; a measurement aid): one launch
  * that reads `bytes` of device memory at `buf` with plain 16-byte loads and
  * nothing else, so that timing it gives the HBM read rate this device
  * sustains, against which the decode's rate can be set.
