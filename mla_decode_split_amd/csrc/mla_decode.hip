@@ -1628,12 +1628,16 @@ struct MergeParams {
 };
 
 // One workgroup of two waves per (sequence, query token, pair of heads); wave w
-// takes head 2j + w and its lane i columns 8i..8i+7 (16-byte loads).  The log-sum-exps and partial outputs of up to kMergeBatch
-// slots are loaded together (none depends on another), then combined with a
-// running maximum, so a sequence of up to kMergeBatch pieces costs one round
-// trip to memory after the index loads.  Partial slot s holds QL query tokens:
-// O at ((s * QL + t) * 16 + h) * 512, LSE at (s * QL + t) * 16 + h.
-constexpr int kMergeBatch = 8;
+// takes head 2j + w and its lane i columns 8i..8i+7 (16-byte loads).  The
+// log-sum-exps and partial outputs of up to NB slots are loaded together (none
+// depends on another), then combined with a running maximum, so a sequence of
+// up to NB pieces costs one round trip to memory after the index loads.  NB is
+// kMergeBatch, or kWideMergeBatch for plans whose sequences have more pieces
+// (known from the host offsets): the wider batch holds twice the registers and
+// issues loads for slots a short sequence does not have, so it is used only
+// there.  Partial slot s holds QL query tokens: O at ((s * QL + t) * 16 + h) *
+// 512, LSE at (s * QL + t) * 16 + h.
+constexpr int kMergeBatch = 8, kWideMergeBatch = 16;
 
 // Range positions g0..g1 of every sequence, derived by the planner from the
 // host kv_indptr and passed with the kernel arguments (read in parallel with
@@ -1649,7 +1653,7 @@ struct NoMergeTable {
   static constexpr bool kHas = false;
 };
 
-template <typename Tab, int QL>
+template <typename Tab, int QL, int NB>
 __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) {
   // two heads per workgroup: wave w of head 2 (blockIdx & 7) + w, 8 columns per lane
   const int bt = blockIdx.x >> 3, h = 2 * (blockIdx.x & 7) + (threadIdx.x >> 6);
@@ -1686,29 +1690,29 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
   if (g0 == g1) return;  // written by stage 1
   float m_run = -INFINITY, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
-  for (int32_t base = g0; base <= g1; base += kMergeBatch) {
+  for (int32_t base = g0; base <= g1; base += NB) {
     // straight-line loads (slots past g1 re-read slot g1 and get weight 0), so
     // that they are all in flight before the first is used
-    float lse[kMergeBatch];
-    u32x4 u[kMergeBatch];
+    float lse[NB];
+    u32x4 u[NB];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < NB; ++k) {
       const int64_t slot = (int64_t)merge_slot(p.cut, std::min(base + k, g1), g0) * QL + tq;
       lse[k] = p.part_lse[slot * kHeads + h];
       u[k] = *(const u32x4*)(p.part_o + (slot * kHeads + h) * kV + 8 * t);
     }
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k)
+    for (int k = 0; k < NB; ++k)
       if (base + k > g1) lse[k] = -INFINITY;
-    f32x4 v[kMergeBatch], v2[kMergeBatch];
+    f32x4 v[NB], v2[NB];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < NB; ++k) {
       v[k] = f32x4{bf_lo(u[k][0]), bf_hi(u[k][0]), bf_lo(u[k][1]), bf_hi(u[k][1])};
       v2[k] = f32x4{bf_lo(u[k][2]), bf_hi(u[k][2]), bf_lo(u[k][3]), bf_hi(u[k][3])};
     }
     float mx = m_run;
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) mx = fmaxf(mx, lse[k]);
+    for (int k = 0; k < NB; ++k) mx = fmaxf(mx, lse[k]);
     // only empty slices so far (mx = -inf): every weight and alpha is 0 and the
     // sums stay 0, with no branch (a branch here lets the compiler hold the
     // partial loads back until the maxima are known)
@@ -1718,7 +1722,7 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     acc *= alpha;
     acc2 *= alpha;
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < NB; ++k) {
       const float wgt = (lse[k] == -INFINITY) ? 0.f : __expf(lse[k] - mref);
       wsum += wgt;
       acc += wgt * v[k];
@@ -1808,6 +1812,7 @@ struct mla_plan {
   size_t lse_offset;
   bool has_table;  // merge ranges known at plan time (host kv_indptr, batch and G small enough)
   MergeTable table;
+  bool wide_merge;  // with the table: some sequence has more than kMergeBatch pieces
   bool has_split_table;  // each workgroup's first piece known at plan time (staged start)
   SplitTable split_table;
 };
@@ -1998,6 +2003,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   const size_t o_bytes = slots * ql * kHeads * kV * sizeof(uint16_t);
   pl->lse_offset = (o_bytes + 255) / 256 * 256;
   pl->has_table = kv_indptr_host && pr->batch_size <= kMergeTable && G < 65536;
+  pl->wide_merge = false;
   if (pl->has_table) {
     for (int b = 0; b < pr->batch_size; ++b) {
       const int64_t s = std::max<int64_t>(kv_indptr_host[b], 0);
@@ -2006,6 +2012,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
       const int64_t g1 = e > s ? cut.pos_of_row(e - 1) : g0 - 1;
       // empty: g0 = 1 > g1 = 0
       pl->table.g01[b] = g1 < g0 ? 1u : (uint32_t)g0 | ((uint32_t)g1 << 16);
+      if (g1 - g0 + 1 > kMergeBatch) pl->wide_merge = true;
     }
   }
   pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
@@ -2179,20 +2186,27 @@ mla_status launch_split_stage(const mla_plan* pl, const SplitParams& sp, hipStre
 mla_status launch_merge_stage(const mla_plan* pl, const MergeParams& mp, hipStream_t st) {
   if (!pl->stage2) return MLA_OK;
   const dim3 grid(pl->prob.batch_size * pl->ql * kHeads / 2), block(128);
-  if (pl->has_table) {
+  if (pl->has_table && pl->wide_merge) {
     if (pl->ql == 1)
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 1>), grid, block, 0, st, mp, pl->table);
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 1, kWideMergeBatch>), grid, block, 0, st, mp, pl->table);
     else if (pl->ql == 2)
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 2>), grid, block, 0, st, mp, pl->table);
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 2, kWideMergeBatch>), grid, block, 0, st, mp, pl->table);
     else
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 4>), grid, block, 0, st, mp, pl->table);
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 4, kWideMergeBatch>), grid, block, 0, st, mp, pl->table);
+  } else if (pl->has_table) {
+    if (pl->ql == 1)
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 1, kMergeBatch>), grid, block, 0, st, mp, pl->table);
+    else if (pl->ql == 2)
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 2, kMergeBatch>), grid, block, 0, st, mp, pl->table);
+    else
+      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 4, kMergeBatch>), grid, block, 0, st, mp, pl->table);
   } else {
     if (pl->ql == 1)
-      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 1>), grid, block, 0, st, mp, NoMergeTable{});
+      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 1, kMergeBatch>), grid, block, 0, st, mp, NoMergeTable{});
     else if (pl->ql == 2)
-      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 2>), grid, block, 0, st, mp, NoMergeTable{});
+      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 2, kMergeBatch>), grid, block, 0, st, mp, NoMergeTable{});
     else
-      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 4>), grid, block, 0, st, mp, NoMergeTable{});
+      hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 4, kMergeBatch>), grid, block, 0, st, mp, NoMergeTable{});
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the merge kernel");
