@@ -1631,13 +1631,13 @@ struct MergeParams {
 // takes head 2j + w and its lane i columns 8i..8i+7 (16-byte loads).  The
 // log-sum-exps and partial outputs of up to NB slots are loaded together (none
 // depends on another), then combined with a running maximum, so a sequence of
-// up to NB pieces costs one round trip to memory after the index loads.  NB is
-// kMergeBatch, or kWideMergeBatch for plans whose sequences have more pieces
-// (known from the host offsets): the wider batch holds twice the registers and
-// issues loads for slots a short sequence does not have, so it is used only
-// there.  Partial slot s holds QL query tokens: O at ((s * QL + t) * 16 + h) *
-// 512, LSE at (s * QL + t) * 16 + h.
-constexpr int kMergeBatch = 8, kWideMergeBatch = 16;
+// up to NB pieces costs one round trip to memory after the index loads.  With
+// the host offsets the plan knows the most pieces any sequence has and picks
+// the smallest NB of 2, 4, 8 and 16 that holds them (a batch issues a load for
+// every one of its NB slots, and the wide batch holds twice the registers);
+// otherwise NB is kMergeBatch.  Partial slot s holds QL query tokens: O at
+// ((s * QL + t) * 16 + h) * 512, LSE at (s * QL + t) * 16 + h.
+constexpr int kMergeBatch = 8;
 
 // Range positions g0..g1 of every sequence, derived by the planner from the
 // host kv_indptr and passed with the kernel arguments (read in parallel with
@@ -1812,7 +1812,7 @@ struct mla_plan {
   size_t lse_offset;
   bool has_table;  // merge ranges known at plan time (host kv_indptr, batch and G small enough)
   MergeTable table;
-  bool wide_merge;  // with the table: some sequence has more than kMergeBatch pieces
+  int32_t merge_batch;  // slots stage 2 loads at once (see mla_merge_kernel)
   bool has_split_table;  // each workgroup's first piece known at plan time (staged start)
   SplitTable split_table;
 };
@@ -2003,7 +2003,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   const size_t o_bytes = slots * ql * kHeads * kV * sizeof(uint16_t);
   pl->lse_offset = (o_bytes + 255) / 256 * 256;
   pl->has_table = kv_indptr_host && pr->batch_size <= kMergeTable && G < 65536;
-  pl->wide_merge = false;
+  int64_t max_pieces = 0;  // the most pieces of one sequence (with the table)
   if (pl->has_table) {
     for (int b = 0; b < pr->batch_size; ++b) {
       const int64_t s = std::max<int64_t>(kv_indptr_host[b], 0);
@@ -2012,9 +2012,10 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
       const int64_t g1 = e > s ? cut.pos_of_row(e - 1) : g0 - 1;
       // empty: g0 = 1 > g1 = 0
       pl->table.g01[b] = g1 < g0 ? 1u : (uint32_t)g0 | ((uint32_t)g1 << 16);
-      if (g1 - g0 + 1 > kMergeBatch) pl->wide_merge = true;
+      max_pieces = std::max<int64_t>(max_pieces, g1 - g0 + 1);
     }
   }
+  pl->merge_batch = !pl->has_table ? kMergeBatch : max_pieces <= 2 ? 2 : max_pieces <= 4 ? 4 : max_pieces <= 8 ? 8 : 16;
   pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
   // Staged start (one query row, contiguous bf16 / fp8 KV): each workgroup's
   // first piece from the host offsets, found by the kernel's own counting rule.
@@ -2183,24 +2184,30 @@ mla_status launch_split_stage(const mla_plan* pl, const SplitParams& sp, hipStre
   return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the split kernel");
 }
 
+extern "C++" {
+template <int QL>
+void launch_merge_nb(const mla_plan* pl, const MergeParams& mp, hipStream_t st) {
+  const dim3 grid(pl->prob.batch_size * pl->ql * kHeads / 2), block(128);
+  switch (pl->merge_batch) {
+    case 2: hipLaunchKernelGGL((mla_merge_kernel<MergeTable, QL, 2>), grid, block, 0, st, mp, pl->table); break;
+    case 4: hipLaunchKernelGGL((mla_merge_kernel<MergeTable, QL, 4>), grid, block, 0, st, mp, pl->table); break;
+    case 16: hipLaunchKernelGGL((mla_merge_kernel<MergeTable, QL, 16>), grid, block, 0, st, mp, pl->table); break;
+    default: hipLaunchKernelGGL((mla_merge_kernel<MergeTable, QL, kMergeBatch>), grid, block, 0, st, mp, pl->table); break;
+  }
+}
+}  // extern "C++"
+
 mla_status launch_merge_stage(const mla_plan* pl, const MergeParams& mp, hipStream_t st) {
   if (!pl->stage2) return MLA_OK;
-  const dim3 grid(pl->prob.batch_size * pl->ql * kHeads / 2), block(128);
-  if (pl->has_table && pl->wide_merge) {
+  if (pl->has_table) {
     if (pl->ql == 1)
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 1, kWideMergeBatch>), grid, block, 0, st, mp, pl->table);
+      launch_merge_nb<1>(pl, mp, st);
     else if (pl->ql == 2)
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 2, kWideMergeBatch>), grid, block, 0, st, mp, pl->table);
+      launch_merge_nb<2>(pl, mp, st);
     else
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 4, kWideMergeBatch>), grid, block, 0, st, mp, pl->table);
-  } else if (pl->has_table) {
-    if (pl->ql == 1)
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 1, kMergeBatch>), grid, block, 0, st, mp, pl->table);
-    else if (pl->ql == 2)
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 2, kMergeBatch>), grid, block, 0, st, mp, pl->table);
-    else
-      hipLaunchKernelGGL((mla_merge_kernel<MergeTable, 4, kMergeBatch>), grid, block, 0, st, mp, pl->table);
+      launch_merge_nb<4>(pl, mp, st);
   } else {
+    const dim3 grid(pl->prob.batch_size * pl->ql * kHeads / 2), block(128);
     if (pl->ql == 1)
       hipLaunchKernelGGL((mla_merge_kernel<NoMergeTable, 1, kMergeBatch>), grid, block, 0, st, mp, NoMergeTable{});
     else if (pl->ql == 2)
