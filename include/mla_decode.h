@@ -119,6 +119,9 @@ typedef struct mla_plan_desc {
                               tile with: 1, 2 or 4 (max_q_len rounded up) */
   int32_t paired_splits;   /* F: 0 for equal ranges, else the CU count (see num_splits) */
   int32_t second_rows_per_split; /* R2 <= R, a multiple of tile_rows: rows of workgroups g >= F when paired */
+  int32_t merge_batch;     /* partial slots stage 2 loads at once: with kv_indptr_host the
+                              smallest of 2, 4, 8, 16 that holds the most slots one sequence
+                              has (16 when more), else 8 */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan;

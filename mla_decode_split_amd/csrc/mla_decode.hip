@@ -2053,6 +2053,7 @@ mla_status mla_decode_plan_describe(const mla_plan* pl, mla_plan_desc* d) {
   d->rows_per_split = (int32_t)pl->cut.ra;
   d->paired_splits = pl->cut.first;
   d->second_rows_per_split = (int32_t)pl->cut.rb;
+  d->merge_batch = pl->merge_batch;
   d->tile_rows = kTile;
   d->stages = pl->stages;
   d->partial_slots = 2 * pl->num_wgs;

@@ -340,3 +340,27 @@ def test_paired_cut(lengths, rows, cus, skew):
     elif paired:
         assert d["paired_splits"] == cus and d["second_rows_per_split"] < d["rows_per_split"]
     _check_cut(plan, ind)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_merge_batch_holds_the_longest_sequence(seed):
+    """Stage 2 loads merge_batch slots at once: with host offsets the smallest
+    of 2, 4, 8 and 16 that holds the most slots any sequence has (16 beyond
+    that), from the stage-2 replay; without them 8."""
+    rng = np.random.default_rng(9100 + seed)
+    lengths = rng.integers(0, 3000, size=int(rng.integers(1, 40)))
+    ind = _indptr(lengths)
+    total = max(int(ind[-1]), 1)
+    rows = int(rng.choice([32, 64, 96, 256, 1024]))
+    plan = _plan(len(lengths), total, "fp8", ind=ind, rows=rows)
+    most = 0
+    for b in range(len(lengths)):
+        slots = np.zeros(64, dtype=np.int32)
+        cnt = ctypes.c_int32(0)
+        st = mla.library().mla_decode_plan_merge_slots(plan.handle, ind.ctypes.data_as(ctypes.c_void_p), b,
+                                                       slots.ctypes.data_as(ctypes.c_void_p), 64, ctypes.byref(cnt))
+        assert st == mla.MLA_OK
+        most = max(most, cnt.value)
+    want = next((nb for nb in (2, 4, 8, 16) if most <= nb), 16)
+    assert mla.mla_decode_plan_describe(plan)["merge_batch"] == want, (most, rows)
+    assert mla.mla_decode_plan_describe(_plan(len(lengths), total, "fp8", rows=rows))["merge_batch"] == 8

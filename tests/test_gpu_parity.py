@@ -184,6 +184,23 @@ def test_forced_split_counts(kv_dtype, rows):
     _check_batch(w, rows_per_split=rows, what=f"forced rows_per_split={rows} kv={kv_dtype}")
 
 
+# (lengths, rows per split, the merge batch the plan picks): stage 2 loads 2,
+# 4, 8 or 16 slots at once, from the most pieces one sequence has; 32-row
+# ranges give up to 32 pieces, two batches of 16
+MERGE_BATCH_CASES = [([300, 200, 60], 256, 2), ([520, 300], 256, 4), ([700, 1000, 33], 224, 8),
+                     ([700, 1000, 33], 96, 16), ([700, 1000, 33], 32, 16)]
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("lengths,rows,nb", MERGE_BATCH_CASES)
+def test_merge_batch_sizes(lengths, rows, nb, kv_dtype, q_len):
+    w = synth.make_batch(lengths, "bf16", kv_dtype, seed=212 + nb, name="merge-batch",
+                         q_lens=None if q_len == 1 else [q_len] * len(lengths))
+    (_, _), plan, _ = _check_batch(w, rows_per_split=rows, what=f"merge batch {nb}, rows {rows}, kv={kv_dtype}, q_len {q_len}")
+    assert mla.mla_decode_plan_describe(plan)["merge_batch"] == nb
+
+
 def test_empty_sequences_give_zero():
     w = synth.make_batch([0, 40, 0, 300, 0], "bf16", "fp8", seed=303, name="empties")
     (_, _), plan, out = _check_batch(w, rows_per_split=64, what="empty sequences")
