@@ -1688,7 +1688,21 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     return;
   }
   if (g0 == g1) return;  // written by stage 1
+  // Every weight is taken against the largest LSE of the sequence: a sequence
+  // of more than NB slots first reads every LSE for it, one of at most NB
+  // slots finds it in its only batch.  With the products added by explicit
+  // fused multiply-adds in slot order, the output does not depend on the batch
+  // size (slots past g1 add exact zeros).
   float m_run = -INFINITY, wsum = 0.f;
+  if (g1 - g0 >= NB)
+    for (int32_t base = g0; base <= g1; base += NB) {
+      float lse[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        lse[k] = p.part_lse[((int64_t)merge_slot(p.cut, std::min(base + k, g1), g0) * QL + tq) * kHeads + h];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) m_run = fmaxf(m_run, lse[k]);
+    }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
   for (int32_t base = g0; base <= g1; base += NB) {
     // straight-line loads (slots past g1 re-read slot g1 and get weight 0), so
@@ -1713,20 +1727,19 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
     float mx = m_run;
 #pragma unroll
     for (int k = 0; k < NB; ++k) mx = fmaxf(mx, lse[k]);
-    // only empty slices so far (mx = -inf): every weight and alpha is 0 and the
-    // sums stay 0, with no branch (a branch here lets the compiler hold the
-    // partial loads back until the maxima are known)
+    // only empty slices (mx = -inf): every weight is 0, with no branch (a
+    // branch here lets the compiler hold the partial loads back until the
+    // maxima are known)
     const float mref = mx == -INFINITY ? 0.f : mx;
-    const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - mref);
-    wsum *= alpha;
-    acc *= alpha;
-    acc2 *= alpha;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const float wgt = (lse[k] == -INFINITY) ? 0.f : __expf(lse[k] - mref);
       wsum += wgt;
-      acc += wgt * v[k];
-      acc2 += wgt * v2[k];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[c] = __builtin_fmaf(wgt, v[k][c], acc[c]);
+        acc2[c] = __builtin_fmaf(wgt, v2[k][c], acc2[c]);
+      }
     }
     m_run = mx;
   }
