@@ -48,9 +48,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "8ba04461e91546e6d600244de3f950d0fd96a7d7312ef448ceba34937573e56e",
-    "fetch_kib": 149904.6,
-    "write_kib": 8226.7,
+    "source_sha256": "638370b99fd484ceaa94021d0cc72902f93411943fe05f326d6eabc860fff421",
+    "fetch_kib": 149904.5,
+    "write_kib": 8225.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
