@@ -96,14 +96,18 @@ typedef struct mla_plan_options {
                              first, and favoured by the hardware), whose ranges are then
                              adjacent (see mla_plan_desc.num_splits): 0 = planner's choice,
                              -1 = equal ranges, 1..500 = that much */
+  int32_t xcd_group;      /* paired ranges: J > 0 puts J consecutive pairs on the CUs of one XCD
+                             (used when the CU count is a multiple of 8 J); 0 = planner's
+                             choice, -1 = pair i on workgroups i and F + i */
 } mla_plan_options;
 
 /* What a plan decided (for tests, benchmarks and logs). */
 typedef struct mla_plan_desc {
   int32_t num_splits;      /* stage-1 workgroups G.  F = paired_splits = 0: workgroup g owns KV rows
-                              [g*R, (g+1)*R).  F > 0 (then G = 2F): workgroups i and F + i - a
-                              CU's first and second - own the rows [i*P, i*P + R) and
-                              [i*P + R, (i+1)*P) with P = R + R2.  Ranges are clipped to total_kv */
+                              [g*R, (g+1)*R).  F > 0 (then G = 2F): workgroups s and F + s - a
+                              CU's first and second - hold pair i (i = s, or see xcd_group) and
+                              own the rows [i*P, i*P + R) and [i*P + R, (i+1)*P) with
+                              P = R + R2.  Ranges are clipped to total_kv */
   int32_t rows_per_split;  /* R, a multiple of tile_rows */
   int32_t tile_rows;       /* KV rows per LDS tile */
   int32_t stages;          /* depth of the LDS tile ring */
@@ -119,6 +123,9 @@ typedef struct mla_plan_desc {
                               tile with: 1, 2 or 4 (max_q_len rounded up) */
   int32_t paired_splits;   /* F: 0 for equal ranges, else the CU count (see num_splits) */
   int32_t second_rows_per_split; /* R2 <= R, a multiple of tile_rows: rows of workgroups g >= F when paired */
+  int32_t xcd_group;       /* paired ranges: J > 0 - workgroups s and F + s hold pair
+                              J * (8 * (k / J) + s % 8) + k % J with k = s / 8 (J consecutive
+                              pairs on one XCD); 0 - they hold pair s */
   int32_t merge_batch;     /* partial slots stage 2 loads at once: with kv_indptr_host the
                               smallest of 2, 4, 8, 16 that holds the most slots one sequence
                               has (16 when more), else 8 */

@@ -223,10 +223,30 @@ struct Ring {
 struct Cut {
   int64_t ra, rb;
   int32_t first, G;
+  // Paired ranges, grp > 0: pairs grp * (8a + x) + j (j < grp) go to the CUs
+  // of XCD x (workgroup slots 8 (grp a + j) + x: consecutive workgroups go to
+  // consecutive XCDs), so grp consecutive pairs - a sequence of grp pairs -
+  // share one XCD's L2.  0: pair i is workgroup slot i.
+  int32_t grp;
   __host__ __device__ int32_t pos_of(int32_t g) const {
-    return first ? (g < first ? 2 * g : 2 * (g - first) + 1) : g;
+    if (!first) return g;
+    const int32_t half = g < first ? 0 : 1;
+    int32_t i = g - half * first;
+    if (grp) {
+      const int32_t k = i / 8, x = i % 8;
+      i = grp * (8 * (k / grp) + x) + k % grp;
+    }
+    return 2 * i + half;
   }
-  __host__ __device__ int32_t wg_at(int32_t pos) const { return first ? ((pos & 1) ? first + (pos >> 1) : pos >> 1) : pos; }
+  __host__ __device__ int32_t wg_at(int32_t pos) const {
+    if (!first) return pos;
+    int32_t i = pos >> 1;
+    if (grp) {
+      const int32_t r = i % (8 * grp);
+      i = 8 * (grp * (i / (8 * grp)) + r % grp) + r / grp;
+    }
+    return (pos & 1) ? first + i : i;
+  }
   __host__ __device__ int64_t lo_at(int32_t pos) const {
     return first ? (int64_t)(pos >> 1) * (ra + rb) + ((pos & 1) ? ra : 0) : (int64_t)pos * ra;
   }
@@ -1950,7 +1970,8 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
     return MLA_ERR_INVALID_ARG;
   if (pr->q_dtype != DT_BF16 && pr->q_dtype != DT_FP8) return MLA_ERR_UNSUPPORTED;
   if (pr->kv_dtype != DT_BF16 && pr->kv_dtype != DT_FP8 && pr->kv_dtype != DT_MXFP4) return MLA_ERR_UNSUPPORTED;
-  if (opt && (opt->rows_per_split < 0 || opt->wgs_per_cu < 0 || opt->age_skew < -1 || opt->age_skew > 500))
+  if (opt && (opt->rows_per_split < 0 || opt->wgs_per_cu < 0 || opt->age_skew < -1 || opt->age_skew > 500 ||
+              opt->xcd_group < -1 || opt->xcd_group > 64))
     return MLA_ERR_INVALID_ARG;
 
   int num_cus = pr->num_cus;
@@ -1984,11 +2005,14 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   // dispatched) takes `skew` per mille of R more rows and the later ones fewer,
   // in whole tiles, so that the later ones - which the SIMD arbiter serves
   // second - finish with it.
-  Cut cut{R, R, 0, (int32_t)G};
+  Cut cut{R, R, 0, (int32_t)G, 0};
   const int skew = opt && opt->age_skew != 0 ? opt->age_skew : kDefaultAgeSkew;
   if (skew > 0 && G == 2 * (int64_t)num_cus) {
     const int64_t d = (R * skew / 1000 + kTile / 2) / kTile * kTile;
-    if (d > 0 && d < R) cut = Cut{R + d, R - d, num_cus, (int32_t)G};
+    if (d > 0 && d < R) {
+      const int grp = opt && opt->xcd_group > 0 ? opt->xcd_group : 0;
+      cut = Cut{R + d, R - d, num_cus, (int32_t)G, grp > 0 && num_cus % (8 * grp) == 0 ? grp : 0};
+    }
   }
 
   bool stage2 = true;
@@ -2066,6 +2090,7 @@ mla_status mla_decode_plan_describe(const mla_plan* pl, mla_plan_desc* d) {
   d->rows_per_split = (int32_t)pl->cut.ra;
   d->paired_splits = pl->cut.first;
   d->second_rows_per_split = (int32_t)pl->cut.rb;
+  d->xcd_group = pl->cut.grp;
   d->merge_batch = pl->merge_batch;
   d->tile_rows = kTile;
   d->stages = pl->stages;

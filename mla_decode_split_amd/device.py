@@ -85,12 +85,12 @@ def upload(w, device="cuda") -> DeviceBatch:
 
 
 def plan_for(batch: DeviceBatch, rows_per_split: int = 0, wgs_per_cu: int = 0, use_host_indptr: bool = True,
-             num_cus: int = 0, age_skew: int = 0) -> Plan:
+             num_cus: int = 0, age_skew: int = 0, xcd_group: int = 0) -> Plan:
     prob = make_problem(batch.batch_size, batch.total_kv, batch.q_dtype, batch.kv_dtype, total_q=batch.total_q,
                         sm_scale=batch.sm_scale, num_cus=num_cus, max_q_len=batch.max_q_len,
                         logit_cap=batch.logit_cap, kv_paged=batch.page_size if batch.kv_indices is not None else 0)
-    opts = mla_plan_options(rows_per_split, wgs_per_cu, age_skew) if (rows_per_split or wgs_per_cu or age_skew) \
-        else None
+    fields = (rows_per_split, wgs_per_cu, age_skew, xcd_group)
+    opts = mla_plan_options(*fields) if any(fields) else None
     return mla_decode_plan(prob, opts, batch.kv_indptr_host if use_host_indptr else None)
 
 

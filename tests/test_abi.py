@@ -75,6 +75,10 @@ def _range(d, g):
         return g * R, (g + 1) * R
     assert d["num_splits"] == 2 * F and R2 % d["tile_rows"] == 0 and 0 < R2 < R
     i = g if g < F else g - F
+    J = d["xcd_group"]
+    if J:  # workgroup slot i holds pair J (8 (k div J) + i mod 8) + k mod J, k = i div 8
+        k = i // 8
+        i = J * (8 * (k // J) + i % 8) + k % J
     lo = i * (R + R2) + (0 if g < F else R)
     return lo, lo + (R if g < F else R2)
 
@@ -364,3 +368,30 @@ def test_merge_batch_holds_the_longest_sequence(seed):
     want = next((nb for nb in (2, 4, 8, 16) if most <= nb), 16)
     assert mla.mla_decode_plan_describe(plan)["merge_batch"] == want, (most, rows)
     assert mla.mla_decode_plan_describe(_plan(len(lengths), total, "fp8", rows=rows))["merge_batch"] == 8
+
+
+@pytest.mark.parametrize("J", [1, 2, 4])
+@pytest.mark.parametrize("lengths,rows,cus", [
+    ([4096] * 64, 1024, 128),                                  # four pairs per sequence
+    ([700, 1000, 33, 1, 2500, 77, 300, 189] * 4 + [1280], 160, 64),  # ragged, pieces crossing pairs
+])
+def test_xcd_grouped_pairs(lengths, rows, cus, J):
+    """Paired ranges with J consecutive pairs on one XCD (consecutive workgroup
+    slots go to consecutive XCDs): the cut still covers every row once and
+    stage 2 merges exactly the partial pieces; pair p sits in a slot on XCD
+    (p div J) mod 8."""
+    ind = _indptr(lengths)
+    prob = mla.make_problem(len(lengths), int(ind[-1]), "bf16", "fp8", num_cus=cus)
+    plan = mla.mla_decode_plan(prob, mla.mla_plan_options(rows, 0, 0, J), ind)
+    d = mla.mla_decode_plan_describe(plan)
+    assert d["paired_splits"] == cus and d["xcd_group"] == J
+    F, R, R2 = cus, d["rows_per_split"], d["second_rows_per_split"]
+    for s in range(F):
+        lo, _ = _range(d, s)
+        p = lo // (R + R2)
+        assert s % 8 == (p // J) % 8
+        assert _range(d, F + s)[0] == lo + R  # the second workgroup of the pair shares the CU
+    _check_cut(plan, ind)
+    # without pairing (or a CU count that is not a multiple of 8 J) there is no grouping
+    flat = mla.mla_decode_plan(prob, mla.mla_plan_options(rows, 0, -1, J), ind)
+    assert mla.mla_decode_plan_describe(flat)["xcd_group"] == 0
