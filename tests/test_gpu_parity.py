@@ -600,3 +600,27 @@ def test_paired_ranges(kv_dtype, q_len, paged, skew):
     torch.cuda.synchronize()
     ref, _ = oracle.decode_workload(w, threads=_host_threads())
     _compare(_bf16_out_to_f64(out), ref, f"paired ranges kv={kv_dtype} q_len={q_len} paged={paged} skew={skew}")
+
+
+@pytest.mark.parametrize("J", [1, 2, 4])
+@pytest.mark.parametrize("kv_dtype,q_len,paged", [("fp8", 1, False), ("bf16", 1, False), ("mxfp4", 1, False),
+                                                  ("fp8", 2, True)])
+def test_xcd_grouped_pairs(kv_dtype, q_len, paged, J):
+    """Paired ranges with J consecutive pairs placed on one XCD's CUs (planned
+    for 32 CUs: 64 ranges of a ragged batch, pieces crossing pair boundaries)
+    against the oracle; the grouping only moves ranges between workgroups, so
+    the output is also bitwise that of the ungrouped plan."""
+    lengths = [700, 1000, 33, 1, 2500, 77, 300, 189] * 2 + [640]
+    w = synth.make_batch(lengths, "bf16", kv_dtype, seed=1414 + J, name="xcd-grouped", q_lens=[q_len] * len(lengths))
+    if paged:
+        w = synth.page_workload(w, seed=1415, spare_rows=200)
+    b = dev.upload(w)
+    plan = dev.plan_for(b, rows_per_split=160, num_cus=32, xcd_group=J)
+    d = mla.mla_decode_plan_describe(plan)
+    assert d["paired_splits"] == 32 and d["num_splits"] == 64 and d["xcd_group"] == J
+    out = dev.run(plan, b, workspace=dev.workspace_for(plan, fill=float("nan")))
+    flat = dev.run(dev.plan_for(b, rows_per_split=160, num_cus=32, xcd_group=-1), b)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), flat.view(torch.int16))
+    ref, _ = oracle.decode_workload(w, threads=_host_threads())
+    _compare(_bf16_out_to_f64(out), ref, f"xcd-grouped pairs J={J} kv={kv_dtype} q_len={q_len} paged={paged}")
