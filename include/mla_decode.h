@@ -61,7 +61,7 @@ typedef struct mla_problem {
   int32_t qk_dim;     /* key width; must be 576 (512 latent + 64 rope) */
   int32_t v_dim;      /* value width; must be 512 (first columns of the KV row) */
   int32_t q_dtype;    /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3FN */
-  int32_t kv_dtype;   /* any mla_dtype; fp8 q requires fp8 KV */
+  int32_t kv_dtype;   /* any mla_dtype, with either q dtype */
   float sm_scale;     /* softmax scale, 1/sqrt(576) for DeepSeek-R1; finite and > 0 */
   int32_t num_cus;    /* compute units to plan for; 0 = ask the current HIP device */
   int32_t max_q_len;  /* query rows per sequence at most (0 or 1: exactly one each; 2..4:
