@@ -48,9 +48,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # reported as null.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "638370b99fd484ceaa94021d0cc72902f93411943fe05f326d6eabc860fff421",
-    "fetch_kib": 149904.5,
-    "write_kib": 8225.0,
+    "source_sha256": "259437c49f9c7af6e8047c3f2583a08cbe2a8e859c47b87a591bcd3def351b70",
+    "fetch_kib": 149906.2,
+    "write_kib": 8225.4,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
