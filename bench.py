@@ -44,11 +44,14 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # HBM bytes of one stage-1 launch on the default workload, from two rocprofv3
 # counter passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
 # what the same counter reads for a plain device copy of 512 MiB.  Valid only
-# for the kernel source they were taken on (its sha256); otherwise traffic is
-# reported as null.
+# for the kernel code they were taken on: the sha256 of the kernel source with
+# its comments removed and its whitespace collapsed (code_sha256 below), so
+# that editing a comment keeps them and changing code drops them (traffic is
+# then reported as null).  The counters were taken on the source whose full
+# sha256 is 259437c4...351b70.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "source_sha256": "259437c49f9c7af6e8047c3f2583a08cbe2a8e859c47b87a591bcd3def351b70",
+    "code_sha256": "13b66fe04c0cea5cf6d79d09c662009b3650be2aa2716dc77fa09353441c564c",
     "fetch_kib": 149906.2,
     "write_kib": 8225.4,
     "fetch_scale": 2.0,
@@ -149,16 +152,39 @@ def cpu_baseline(w, kv_bytes_per_row: float, target_s: float) -> dict:
     return res
 
 
-def _source_sha256() -> str:
+def code_sha256(path: str = KERNEL_SRC) -> str:
+    """sha256 of a C++ source with its comments removed (string and character
+    literals kept as they are) and every run of whitespace collapsed to one
+    space."""
     import hashlib
 
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    text = open(path, encoding="utf-8").read()
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # a literal: copied up to its closing quote
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    code = " ".join("".join(out).split())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def _measured_traffic(name: str):
     t = TRAFFIC_MEASURED
-    if name != t["workload"] or not t["source_sha256"] or t["source_sha256"] != _source_sha256():
+    if name != t["workload"] or not t["code_sha256"] or t["code_sha256"] != code_sha256():
         return None
     return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
 

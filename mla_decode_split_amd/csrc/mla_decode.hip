@@ -11,13 +11,17 @@
 // exp(lse_s - max lse).  Submission 739756's HIP kernel is prior art for the
 // LDS-staged MFMA pipeline; the design below is our own for gfx950.
 //
-// Work decomposition.  The KV rows [0, total_kv) are cut into G equal ranges of
-// R rows; workgroup g owns rows [g*R, (g+1)*R).  Because sequences are stored
-// back to back (kv_indptr is a CSR offset array), a range covers pieces of one
-// or more sequences.  A sequence that lies wholly inside one range is written
-// to `out` directly; a piece of a longer sequence goes to partial slot
-// 2g + (piece starts before the range ? 0 : 1), and stage 2 merges those.  This
-// balances rows, not sequences, so ragged batches keep every CU equally busy.
+// Work decomposition.  The KV rows [0, total_kv) are cut into G ranges in row
+// order: equal ranges of R rows, or - with two workgroups per CU - pairs of a
+// longer range for the CU's older workgroup and a shorter one for its younger
+// (Cut).  Because sequences are stored back to back (kv_indptr is a CSR offset
+// array), a range covers pieces of one or more sequences.  With the host
+// offsets the plan passes each workgroup's first piece in the kernel
+// arguments, so its first KV tile goes out before any other load.  A sequence
+// that lies wholly inside one range is written to `out` directly; a piece of a
+// longer sequence goes to partial slot 2g + (piece starts before the range ? 0
+// : 1), and stage 2 merges those.  This balances rows, not sequences, so
+// ragged batches keep every CU equally busy.
 //
 // Stage-1 workgroup (one query row per sequence): four wave64s (two workgroups
 // per CU for bf16 and fp8 KV, three for MXFP4; one wave of each on every SIMD)
