@@ -129,6 +129,13 @@ typedef struct mla_plan_desc {
   int32_t merge_batch;     /* partial slots stage 2 loads at once: with kv_indptr_host the
                               smallest of 2, 4, 8, 16 that holds the most slots one sequence
                               has (16 when more), else 8 */
+  int32_t first_piece_table; /* 1: each stage-1 workgroup's first piece was derived from
+                              kv_indptr_host and travels with the kernel arguments, so its first
+                              KV tile (and its query row) are requested before any other load.
+                              Planned with kv_indptr_host, one query row per sequence, contiguous
+                              bf16 or fp8 KV, kv_indptr_host[0] = 0, at most 640 workgroups,
+                              batch <= 2^14 and rows per workgroup < 2^16; else 0 (the kernel
+                              searches kv_indptr) */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan;

@@ -41,7 +41,8 @@ class mla_plan_desc(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("wgs_per_cu", ctypes.c_int32), ("query_tokens", ctypes.c_int32),
                 ("paired_splits", ctypes.c_int32), ("second_rows_per_split", ctypes.c_int32),
-                ("xcd_group", ctypes.c_int32), ("merge_batch", ctypes.c_int32)]
+                ("xcd_group", ctypes.c_int32), ("merge_batch", ctypes.c_int32),
+                ("first_piece_table", ctypes.c_int32)]
 
 
 class MlaError(RuntimeError):

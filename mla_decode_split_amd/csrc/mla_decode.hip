@@ -2096,6 +2096,7 @@ mla_status mla_decode_plan_describe(const mla_plan* pl, mla_plan_desc* d) {
   d->second_rows_per_split = (int32_t)pl->cut.rb;
   d->xcd_group = pl->cut.grp;
   d->merge_batch = pl->merge_batch;
+  d->first_piece_table = pl->has_split_table ? 1 : 0;
   d->tile_rows = kTile;
   d->stages = pl->stages;
   d->partial_slots = 2 * pl->num_wgs;

@@ -571,6 +571,8 @@ def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows):
     b = dev.upload(w)
     staged = dev.plan_for(b, rows_per_split=rows, use_host_indptr=True)
     searched = dev.plan_for(b, rows_per_split=rows, use_host_indptr=False)
+    assert mla.mla_decode_plan_describe(staged)["first_piece_table"] == 1
+    assert mla.mla_decode_plan_describe(searched)["first_piece_table"] == 0
     o1 = dev.run(staged, b)
     o2 = dev.run(searched, b)
     torch.cuda.synchronize()
