@@ -1539,7 +1539,27 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
   const float out_scale = ks;
 
   int b_first, b_end;
-  if constexpr (Tab::kHas) {
+  if constexpr (Tab::kHas && PAGED) {
+    // Paged KV with pages of one row: the first piece from the table, so the
+    // index and query loads go out without the kv_indptr search first (the
+    // piece's CSR rows are its kv_indices entries).
+    static_assert(QL == 1 && KF != DT_MXFP4, "first-piece table: one query row, bf16 / fp8 KV");
+    const uint32_t v = tab.first[gi];
+    const int n_first = (int)(v & 0xffffu);
+    const int b0 = (int)((v >> 16) & 0x3fffu);
+    if (n_first > 0) {
+      const int64_t s0 = (v >> 30) & 1u ? lo : lo - 1;  // only "before lo" matters below lo
+      const int64_t e0 = (v >> 31) ? lo + n_first : hi + 1;
+      split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab,
+                                          b0, 1, lo, n_first,
+                                          piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, (int32_t)(hi - lo),
+                                          PageSpan{lo, p.total_kv - lo, 0}, false);
+      lds_barrier();  // the next piece refills the ring
+    }
+    if (n_first == 0 || lo + n_first >= hi) return;
+    b_first = b0 + 1;
+    b_end = p.batch;  // pieces until one starts at or past hi
+  } else if constexpr (Tab::kHas) {
     // Staged start: tile 0 of the first piece (which starts at lo) goes out at
     // once, then - with the piece's sequence from the table - that sequence's
     // query row into the ring's last slot, then tiles 1 .. NS - 2; the piece
@@ -1905,7 +1925,7 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 template <int QF, int KF, bool CAP, bool PAGED>
 void launch_split_v(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
   const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads * (pl->ql == 4 ? RowSplit<4>::kGroups : 1));
-  if constexpr (!PAGED && KF != DT_MXFP4) {
+  if constexpr (KF != DT_MXFP4) {
     if (pl->ql == 1 && pl->has_split_table) {
       hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, SplitTable>), grid, block, 0, st, sp,
                          pl->split_table);
@@ -2060,7 +2080,7 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
   // Staged start (one query row, contiguous bf16 / fp8 KV): each workgroup's
   // first piece from the host offsets, found by the kernel's own counting rule.
-  pl->has_split_table = kv_indptr_host && ql == 1 && !pr->kv_paged && pr->kv_dtype != DT_MXFP4 &&
+  pl->has_split_table = kv_indptr_host && ql == 1 && pr->kv_paged <= 1 && pr->kv_dtype != DT_MXFP4 &&
                         kv_indptr_host[0] == 0 && G <= kSplitTable && pr->batch_size <= (1 << 14) && cut.ra < (1 << 16);
   if (pl->has_split_table) {
     const int32_t* ind = kv_indptr_host;
