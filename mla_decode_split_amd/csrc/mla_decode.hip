@@ -1500,10 +1500,10 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
 // no rows of any sequence), its sequence (bits 16-29), whether the sequence
 // starts at the range's first row (bit 30) and whether it ends inside the
 // range (bit 31).  The piece always starts at the range's first row.  Used with
-// one query row per sequence and contiguous bf16 or fp8 KV, when the plan
+// one query row per sequence and contiguous KV or pages of one row, when the plan
 // knows the offsets, kv_indptr[0] = 0, G <= kSplitTable, batch <= 2^14 and
 // R < 2^16.
-constexpr int kSplitTable = 640;
+constexpr int kSplitTable = 768;
 struct SplitTable {
   static constexpr bool kHas = true;
   uint32_t first[kSplitTable];
@@ -1511,6 +1511,7 @@ struct SplitTable {
 struct NoSplitTable {
   static constexpr bool kHas = false;
 };
+static_assert(sizeof(SplitParams) + sizeof(SplitTable) <= 4096, "kernel arguments within 4 KB");
 
 template <int QF, int KF, int QL, bool CAP, bool PAGED, typename Tab>
 __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attribute__((amdgpu_waves_per_eu(
@@ -1539,11 +1540,13 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
   const float out_scale = ks;
 
   int b_first, b_end;
-  if constexpr (Tab::kHas && PAGED) {
-    // Paged KV with pages of one row: the first piece from the table, so the
-    // index and query loads go out without the kv_indptr search first (the
-    // piece's CSR rows are its kv_indices entries).
-    static_assert(QL == 1 && KF != DT_MXFP4, "first-piece table: one query row, bf16 / fp8 KV");
+  if constexpr (Tab::kHas && (PAGED || KF == DT_MXFP4)) {
+    // Paged KV with pages of one row, and MXFP4 KV: the first piece from the
+    // table, so its loads (indices, query) go out without the kv_indptr search
+    // first (a paged piece's CSR rows are its kv_indices entries).  MXFP4 tiles
+    // are not issued before the query: there the first tiles of every
+    // workgroup together, not the search, bound the start.
+    static_assert(QL == 1, "first-piece table: one query row");
     const uint32_t v = tab.first[gi];
     const int n_first = (int)(v & 0xffffu);
     const int b0 = (int)((v >> 16) & 0x3fffu);
@@ -1925,7 +1928,7 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 template <int QF, int KF, bool CAP, bool PAGED>
 void launch_split_v(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
   const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads * (pl->ql == 4 ? RowSplit<4>::kGroups : 1));
-  if constexpr (KF != DT_MXFP4) {
+  {
     if (pl->ql == 1 && pl->has_split_table) {
       hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, SplitTable>), grid, block, 0, st, sp,
                          pl->split_table);
@@ -2078,9 +2081,9 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   }
   pl->merge_batch = !pl->has_table ? kMergeBatch : max_pieces <= 2 ? 2 : max_pieces <= 4 ? 4 : max_pieces <= 8 ? 8 : 16;
   pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
-  // Staged start (one query row, contiguous bf16 / fp8 KV): each workgroup's
+  // First-piece table (one query row, contiguous KV or pages of one row): each workgroup's
   // first piece from the host offsets, found by the kernel's own counting rule.
-  pl->has_split_table = kv_indptr_host && ql == 1 && pr->kv_paged <= 1 && pr->kv_dtype != DT_MXFP4 &&
+  pl->has_split_table = kv_indptr_host && ql == 1 && pr->kv_paged <= 1 &&
                         kv_indptr_host[0] == 0 && G <= kSplitTable && pr->batch_size <= (1 << 14) && cut.ra < (1 << 16);
   if (pl->has_split_table) {
     const int32_t* ind = kv_indptr_host;

@@ -65,31 +65,30 @@ def test_plans_for_the_five_workloads(name):
     assert d["lds_bytes"] * d["wgs_per_cu"] <= 160 * 1024  # that many workgroups fit a CU's LDS
     assert d["wgs_per_cu"] == (3 if spec["kv_dtype"] == "mxfp4" else 2)
     assert plan.workspace_bytes >= d["partial_slots"] * 16 * (512 * 2 + 4)  # bf16 O + fp32 LSE per head
-    # stage 1 starts from the plan's first pieces with bf16 and fp8 KV
-    assert d["first_piece_table"] == (0 if spec["kv_dtype"] == "mxfp4" else 1)
+    assert d["first_piece_table"] == 1  # stage 1 starts from the plan's first pieces
     _check_cut(plan, ind)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 def test_first_piece_table_conditions(kv):
     """The first-piece table goes with the kernel arguments only when the plan
-    has the host offsets, one query row per sequence, bf16 or fp8 KV (contiguous
-    or in pages of one row) and at most 640 workgroups."""
+    has the host offsets, one query row per sequence, contiguous KV or pages of
+    one row, and at most 768 workgroups."""
     lengths = [300, 0, 1000, 7, 2048]
     ind = _indptr(lengths)
     total = int(ind[-1])
     desc = lambda plan: mla.mla_decode_plan_describe(plan)
-    want = 0 if kv == "mxfp4" else 1
+    want = 1
     assert desc(_plan(len(lengths), total, kv, ind=ind, rows=64))["first_piece_table"] == want
     assert desc(_plan(len(lengths), total, kv, ind=None, rows=64))["first_piece_table"] == 0
     assert desc(_plan(len(lengths), total, kv, ind=ind, rows=64, kv_paged=1))["first_piece_table"] == want
     assert desc(_plan(len(lengths), total, kv, ind=ind, rows=64, kv_paged=16))["first_piece_table"] == 0
     q2 = mla.make_problem(len(lengths), total, "bf16", kv, num_cus=256, total_q=2 * len(lengths), max_q_len=2)
     assert desc(mla.mla_decode_plan(q2, mla.mla_plan_options(64, 0), ind))["first_piece_table"] == 0
-    # 640 workgroups fit the table, 641 do not
-    many = [32] * 641
-    assert desc(_plan(640, 640 * 32, kv, ind=_indptr(many[:640]), rows=32))["first_piece_table"] == want
-    assert desc(_plan(641, 641 * 32, kv, ind=_indptr(many), rows=32))["first_piece_table"] == 0
+    # 768 workgroups fit the table, 769 do not
+    many = [32] * 769
+    assert desc(_plan(768, 768 * 32, kv, ind=_indptr(many[:768]), rows=32))["first_piece_table"] == want
+    assert desc(_plan(769, 769 * 32, kv, ind=_indptr(many), rows=32))["first_piece_table"] == 0
 
 
 def _range(d, g):

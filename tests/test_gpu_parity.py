@@ -555,7 +555,8 @@ def test_workload_parity_at_full_size(name):
 
 # ------------------------------------------------------------- staged start
 
-@pytest.mark.parametrize("q_dtype,kv_dtype", [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8"), ("fp8", "bf16")])
+@pytest.mark.parametrize("q_dtype,kv_dtype", [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8"), ("fp8", "bf16"),
+                                             ("bf16", "mxfp4"), ("fp8", "mxfp4")])
 @pytest.mark.parametrize("rows", [32, 64, 96, 1024])
 @pytest.mark.parametrize("paged", [False, True])
 def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows, paged):
@@ -570,6 +571,8 @@ def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows, paged):
     w = synth.make_batch(lengths, q_dtype, kv_dtype, seed=909 + rows, name="staged")
     extra = synth.make_batch([3 * rows + 17], "bf16", kv_dtype, seed=910, name="tail")
     w.kv = np.concatenate([w.kv, extra.kv])  # rows no sequence uses
+    if kv_dtype == "mxfp4":
+        w.kv_scale = np.concatenate([w.kv_scale, extra.kv_scale])  # and their E8M0 rows
     if paged:
         w = synth.page_workload(w, seed=911 + rows, spare_rows=150)
     b = dev.upload(w)
