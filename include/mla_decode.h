@@ -133,12 +133,12 @@ typedef struct mla_plan_desc {
                               kv_indptr_host and travels with the kernel arguments, so its first
                               loads go out without a kv_indptr search: with contiguous bf16 or
                               fp8 KV its first KV tile and its query row, before any other load;
-                              with MXFP4 KV or pages of one row its query row and its first KV
-                              tiles (or their kv_indices entries).
-                              Planned with kv_indptr_host, one query row per sequence, KV
-                              contiguous or in pages of one row, kv_indptr_host[0] = 0, at most
-                              768 workgroups, batch <= 2^14 and rows per workgroup < 2^16; else 0
-                              (the kernel searches kv_indptr) */
+                              with MXFP4 KV or paged KV its query row and its first KV tiles (or
+                              their kv_indices entries; with pages of more than one row after one
+                              round trip for the sequence's page list).
+                              Planned with kv_indptr_host, one query row per sequence,
+                              kv_indptr_host[0] = 0, at most 768 workgroups, batch <= 2^14 and
+                              rows per workgroup < 2^16; else 0 (the kernel searches kv_indptr) */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan;

@@ -1500,7 +1500,7 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
 // no rows of any sequence), its sequence (bits 16-29), whether the sequence
 // starts at the range's first row (bit 30) and whether it ends inside the
 // range (bit 31).  The piece always starts at the range's first row.  Used with
-// one query row per sequence and contiguous KV or pages of one row, when the plan
+// one query row per sequence, when the plan
 // knows the offsets, kv_indptr[0] = 0, G <= kSplitTable, batch <= 2^14 and
 // R < 2^16.
 constexpr int kSplitTable = 768;
@@ -1541,11 +1541,12 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
 
   int b_first, b_end;
   if constexpr (Tab::kHas && (PAGED || KF == DT_MXFP4)) {
-    // Paged KV with pages of one row, and MXFP4 KV: the first piece from the
-    // table, so its loads (indices, query) go out without the kv_indptr search
-    // first (a paged piece's CSR rows are its kv_indices entries).  MXFP4 tiles
-    // are not issued before the query: there the first tiles of every
-    // workgroup together, not the search, bound the start.
+    // Paged KV and MXFP4 KV: the first piece from the table, so its loads
+    // (indices, query) go out without the kv_indptr search first.  With pages
+    // of one row a piece's CSR rows are its kv_indices entries; with larger
+    // pages the sequence's page list and first row come in one round trip.
+    // MXFP4 tiles are not issued before the query: there the first tiles of
+    // every workgroup together, not the search, bound the start.
     static_assert(QL == 1, "first-piece table: one query row");
     const uint32_t v = tab.first[gi];
     const int n_first = (int)(v & 0xffffu);
@@ -1553,10 +1554,18 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
     if (n_first > 0) {
       const int64_t s0 = (v >> 30) & 1u ? lo : lo - 1;  // only "before lo" matters below lo
       const int64_t e0 = (v >> 31) ? lo + n_first : hi + 1;
+      PageSpan ps{lo, p.total_kv - lo, 0};
+      if (PAGED && p.page_shift) {
+        const int32_t s_raw = p.kv_indptr[b0], pb_raw = p.kv_page_indptr[b0], pe_raw = p.kv_page_indptr[b0 + 1];
+        const int64_t s = uniform(s_raw), pb = uniform(pb_raw), pe = uniform(pe_raw);
+        // a page list that cannot be read is read as empty (all pages 0)
+        const bool ok = pb >= 0 && pe >= pb;
+        ps = PageSpan{ok ? pb : 0, ok ? pe - pb : 0, (int32_t)(lo - s)};
+      }
       split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab,
                                           b0, 1, lo, n_first,
                                           piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, (int32_t)(hi - lo),
-                                          PageSpan{lo, p.total_kv - lo, 0}, false);
+                                          ps, false);
       lds_barrier();  // the next piece refills the ring
     }
     if (n_first == 0 || lo + n_first >= hi) return;
@@ -2081,9 +2090,9 @@ mla_status mla_decode_plan(const mla_problem* pr, const mla_plan_options* opt, c
   }
   pl->merge_batch = !pl->has_table ? kMergeBatch : max_pieces <= 2 ? 2 : max_pieces <= 4 ? 4 : max_pieces <= 8 ? 8 : 16;
   pl->ws_bytes = pl->lse_offset + (slots * ql * kHeads * sizeof(float) + 255) / 256 * 256;
-  // First-piece table (one query row, contiguous KV or pages of one row): each workgroup's
+  // First-piece table (one query row): each workgroup's
   // first piece from the host offsets, found by the kernel's own counting rule.
-  pl->has_split_table = kv_indptr_host && ql == 1 && pr->kv_paged <= 1 &&
+  pl->has_split_table = kv_indptr_host && ql == 1 &&
                         kv_indptr_host[0] == 0 && G <= kSplitTable && pr->batch_size <= (1 << 14) && cut.ra < (1 << 16);
   if (pl->has_split_table) {
     const int32_t* ind = kv_indptr_host;

@@ -72,8 +72,8 @@ def test_plans_for_the_five_workloads(name):
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 def test_first_piece_table_conditions(kv):
     """The first-piece table goes with the kernel arguments only when the plan
-    has the host offsets, one query row per sequence, contiguous KV or pages of
-    one row, and at most 768 workgroups."""
+    has the host offsets, one query row per sequence and at most 768
+    workgroups."""
     lengths = [300, 0, 1000, 7, 2048]
     ind = _indptr(lengths)
     total = int(ind[-1])
@@ -82,7 +82,7 @@ def test_first_piece_table_conditions(kv):
     assert desc(_plan(len(lengths), total, kv, ind=ind, rows=64))["first_piece_table"] == want
     assert desc(_plan(len(lengths), total, kv, ind=None, rows=64))["first_piece_table"] == 0
     assert desc(_plan(len(lengths), total, kv, ind=ind, rows=64, kv_paged=1))["first_piece_table"] == want
-    assert desc(_plan(len(lengths), total, kv, ind=ind, rows=64, kv_paged=16))["first_piece_table"] == 0
+    assert desc(_plan(len(lengths), total, kv, ind=ind, rows=64, kv_paged=16))["first_piece_table"] == want
     q2 = mla.make_problem(len(lengths), total, "bf16", kv, num_cus=256, total_q=2 * len(lengths), max_q_len=2)
     assert desc(mla.mla_decode_plan(q2, mla.mla_plan_options(64, 0), ind))["first_piece_table"] == 0
     # 768 workgroups fit the table, 769 do not
@@ -303,11 +303,7 @@ def test_page_sizes_share_the_paged_plan(kv_dtype):
     for P in (2, 16, 64, 1024, 65536):
         plan = mla.mla_decode_plan(mla.make_problem(4, int(ind[-1]), "bf16", kv_dtype, num_cus=256, kv_paged=P),
                                    None, ind)
-        d = mla.mla_decode_plan_describe(plan)
-        # the first-piece table is for pages of one row only
-        assert d["first_piece_table"] == 0
-        d["first_piece_table"] = base["first_piece_table"]
-        assert d == base
+        assert mla.mla_decode_plan_describe(plan) == base
         _check_cut(plan, ind)
 
 

@@ -558,23 +558,27 @@ def test_workload_parity_at_full_size(name):
 @pytest.mark.parametrize("q_dtype,kv_dtype", [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8"), ("fp8", "bf16"),
                                              ("bf16", "mxfp4"), ("fp8", "mxfp4")])
 @pytest.mark.parametrize("rows", [32, 64, 96, 1024])
-@pytest.mark.parametrize("paged", [False, True])
-def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows, paged):
+@pytest.mark.parametrize("page", [0, 1, 16])
+def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows, page):
     """A plan made with the host offsets starts each stage-1 workgroup from a
     table of first pieces (tile 0, the query row and the rest of the ring
     prologue issued before any other load); a plan without them searches
     kv_indptr.  Same cut, same bits: sequences shorter than the ring, starting
     exactly at a range boundary, empty ones, and KV rows past the last sequence
-    (workgroups with no piece at all).  Paged (pages of one row): the table
-    gives the first piece, whose index and query loads then go out at once."""
+    (workgroups with no piece at all).  Paged KV (page > 0 rows per page): the
+    table gives the first piece, whose index and query loads then go out at
+    once."""
     lengths = [1, 31, 32, 33, 64, 0, 200, 1000, 5, 96, 0, 2, 700]
     w = synth.make_batch(lengths, q_dtype, kv_dtype, seed=909 + rows, name="staged")
-    extra = synth.make_batch([3 * rows + 17], "bf16", kv_dtype, seed=910, name="tail")
-    w.kv = np.concatenate([w.kv, extra.kv])  # rows no sequence uses
-    if kv_dtype == "mxfp4":
-        w.kv_scale = np.concatenate([w.kv_scale, extra.kv_scale])  # and their E8M0 rows
-    if paged:
-        w = synth.page_workload(w, seed=911 + rows, spare_rows=150)
+    if page <= 1:
+        # CSR rows no sequence uses (with pages of several rows the CSR space
+        # ends with the last sequence)
+        extra = synth.make_batch([3 * rows + 17], "bf16", kv_dtype, seed=910, name="tail")
+        w.kv = np.concatenate([w.kv, extra.kv])
+        if kv_dtype == "mxfp4":
+            w.kv_scale = np.concatenate([w.kv_scale, extra.kv_scale])  # and their E8M0 rows
+    if page:
+        w = synth.page_workload(w, seed=911 + rows, spare_rows=150, page_size=page)
     b = dev.upload(w)
     staged = dev.plan_for(b, rows_per_split=rows, use_host_indptr=True)
     searched = dev.plan_for(b, rows_per_split=rows, use_host_indptr=False)
@@ -585,7 +589,7 @@ def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows, paged):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     ref, _ = oracle.decode_workload(w, threads=_host_threads())
-    _compare(_bf16_out_to_f64(o1), ref, f"staged start {q_dtype}/{kv_dtype} rows {rows} paged {paged}")
+    _compare(_bf16_out_to_f64(o1), ref, f"staged start {q_dtype}/{kv_dtype} rows {rows} page {page}")
 
 
 # ------------------------------------------------------------- paired ranges
