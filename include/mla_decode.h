@@ -136,9 +136,11 @@ typedef struct mla_plan_desc {
                               with MXFP4 KV or paged KV its query row and its first KV tiles (or
                               their kv_indices entries; with pages of more than one row after one
                               round trip for the sequence's page list).
-                              Planned with kv_indptr_host, one query row per sequence,
-                              kv_indptr_host[0] = 0, at most 768 workgroups, batch <= 2^14 and
-                              rows per workgroup < 2^16; else 0 (the kernel searches kv_indptr) */
+                              Planned with kv_indptr_host, one query row per sequence (then
+                              qo_indptr[b] = b, which the run's contract implies, and the first
+                              piece's query row is taken to be row b), kv_indptr_host[0] = 0, at
+                              most 768 workgroups, batch <= 2^14 and rows per workgroup < 2^16;
+                              else 0 (the kernel searches kv_indptr) */
 } mla_plan_desc;
 
 typedef struct mla_plan mla_plan;
