@@ -592,6 +592,31 @@ def test_staged_start_equals_searched_start(q_dtype, kv_dtype, rows, page):
     _compare(_bf16_out_to_f64(o1), ref, f"staged start {q_dtype}/{kv_dtype} rows {rows} page {page}")
 
 
+@pytest.mark.parametrize("kv_dtype", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("groups", [768, 769])
+def test_first_piece_table_at_its_limit(kv_dtype, groups):
+    """768 stage-1 workgroups carry the first-piece table in the kernel
+    arguments, 769 do not: both against the searched start bit for bit and
+    against the oracle, with ragged sequences over 32-row ranges."""
+    rng = np.random.default_rng(4242 + groups)
+    total = groups * 32 - 5
+    cuts = np.sort(rng.choice(np.arange(1, total), size=40, replace=False))
+    lengths = np.diff(np.concatenate([[0], cuts, [total]])).tolist()
+    w = synth.make_batch(lengths, "bf16", kv_dtype, seed=4243 + groups, name="table_limit")
+    b = dev.upload(w)
+    table = dev.plan_for(b, rows_per_split=32, use_host_indptr=True)
+    searched = dev.plan_for(b, rows_per_split=32, use_host_indptr=False)
+    d = mla.mla_decode_plan_describe(table)
+    assert d["num_splits"] == groups
+    assert d["first_piece_table"] == (1 if groups <= 768 else 0)
+    o1 = dev.run(table, b)
+    o2 = dev.run(searched, b)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    ref, _ = oracle.decode_workload(w, threads=_host_threads())
+    _compare(_bf16_out_to_f64(o1), ref, f"first-piece table, {groups} workgroups, {kv_dtype}")
+
+
 # ------------------------------------------------------------- paired ranges
 
 @pytest.mark.parametrize("skew", [120, 250])
