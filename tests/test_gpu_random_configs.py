@@ -66,7 +66,7 @@ def _draw(seed):
     return dict(lengths=lengths, q_dtype=q_dtype, kv_dtype=kv_dtype, q_lens=q_lens, cap=cap, page=page, opts=opts)
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(200))
 def test_random_config(seed):
     c = _draw(seed)
     what = (f"random #{seed}: bs={len(c['lengths'])} rows={int(c['lengths'].sum())} {c['q_dtype']}/{c['kv_dtype']} "
