@@ -333,6 +333,21 @@ mla_status mla_debug_decode(int32_t kv_dtype, const void* codes, const void* sca
  */
 mla_status mla_debug_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Per-workgroup timeline of the last stage-1 launch (a measurement aid, defined
+ * by none of the pages; for finding where a call's time goes).  Only the
+ * library built with -DMLA_WG_TRACE records it (mla_decode_split_amd/build.py,
+ * build_trace); the product build returns MLA_ERR_UNSUPPORTED and its kernels
+ * carry no part of it.  Entry g of the host array (4 uint64 per stage-1
+ * workgroup g < 8192): start, first KV tile complete in LDS, end, all on the
+ * device's 100 MHz real-time counter, and the XCC_ID | HW_ID << 8 register
+ * values of the CU it ran on.  Workgroups that own no rows write nothing.
+ *   host   receives the first n uint64 entries (n <= 4 * 8192); may be NULL when n = 0.
+ *   clear  nonzero: zero the record first (before a launch to be traced).
+ * Synchronous (device-wide copies).
+ */
+mla_status mla_debug_wg_trace(uint64_t* host, int64_t n, int32_t clear);
+
 /* Human-readable status name. */
 const char* mla_status_string(mla_status status);
 

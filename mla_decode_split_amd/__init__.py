@@ -91,6 +91,8 @@ def _lib_handle():
         lib.mla_debug_decode.restype = i32
         lib.mla_debug_stream_read.argtypes = [vp, i64, vp, vp]
         lib.mla_debug_stream_read.restype = i32
+        lib.mla_debug_wg_trace.argtypes = [vp, i64, i32]
+        lib.mla_debug_wg_trace.restype = i32
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_last_error_string.argtypes = []
@@ -282,3 +284,14 @@ def mla_debug_stream_read(buf, nbytes: int, sink, stream=None) -> None:
     st = _lib_handle().mla_debug_stream_read(_addr(buf), nbytes, _addr(sink), _stream(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_debug_stream_read")
+
+
+def mla_debug_wg_trace(host: np.ndarray | None, clear: bool = False) -> None:
+    """Copy the stage-1 workgroup timeline into `host` (uint64, 4 per workgroup)
+    and/or clear it; the library must be the MLA_WG_TRACE build."""
+    n = 0 if host is None else int(host.size)
+    if host is not None and (host.dtype != np.uint64 or not host.flags["C_CONTIGUOUS"]):
+        raise ValueError("host must be a contiguous uint64 array")
+    st = _lib_handle().mla_debug_wg_trace(None if host is None else host.ctypes.data, n, 1 if clear else 0)
+    if st != MLA_OK:
+        raise MlaError(st, "mla_debug_wg_trace")

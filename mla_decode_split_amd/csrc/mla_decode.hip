@@ -675,6 +675,22 @@ __device__ inline void load_vt(const uint8_t* st, const LaneOffs<KF>& lo, int q,
 
 // ---------------------------------------------------------------- stage 1
 
+#ifdef MLA_WG_TRACE
+// Measurement build only (-DMLA_WG_TRACE; the product build has none of it):
+// the timeline of each stage-1 workgroup of the last launch, read back with
+// mla_debug_wg_trace.  Entry g: [0] start (after the range check), [1] its
+// first tile complete in LDS, [2] end, all on the 100 MHz real-time counter,
+// and [3] the XCC_ID register | the HW_ID register << 8.
+constexpr int kWgTraceMax = 8192;
+__device__ uint64_t g_wg_trace[kWgTraceMax * 4];
+struct WgTraceEnd {
+  int32_t g;
+  __device__ ~WgTraceEnd() {
+    if (threadIdx.x == 0 && g < kWgTraceMax) g_wg_trace[4 * g + 2] = __builtin_amdgcn_s_memrealtime();
+  }
+};
+#endif
+
 struct SplitParams {
   const uint8_t* q;
   const float* q_scale;
@@ -1426,6 +1442,10 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   // tile 0, then for each later tile: its scores and the previous tile's products
   priority(0);
   advance(0);
+#ifdef MLA_WG_TRACE
+  if (threadIdx.x == 0 && blockIdx.x < kWgTraceMax && g_wg_trace[4 * blockIdx.x + 1] == 0)
+    g_wg_trace[4 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+#endif
   idx_step(0);
   if (nfull > 0)
     score_tile<QF, KF, QW, NG, CAP, PAGED, false>(stage(0), pbuf_of(0), xchg, qop, lo, ws, w, w8, tb, m, g, scales_of(0), kTile, cs, cap, ts);
@@ -1532,6 +1552,14 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
   const int64_t lo = p.cut.lo_at(pos);
   const int64_t hi = std::min<int64_t>(p.cut.lo_at(pos + 1), p.total_kv);
   if (lo >= hi) return;
+#ifdef MLA_WG_TRACE
+  if (tid == 0 && gi < kWgTraceMax) {
+    g_wg_trace[4 * gi + 0] = __builtin_amdgcn_s_memrealtime();
+    g_wg_trace[4 * gi + 3] = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) |
+                             ((uint64_t)__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11)) << 8);
+  }
+  const WgTraceEnd trace_end{gi};
+#endif
 
   float qs = 1.f, ks = 1.f;
   if (QF == DT_FP8) qs = *p.q_scale;
@@ -2437,6 +2465,25 @@ mla_status mla_debug_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
                      bytes / 16, sink);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the read-ceiling kernel");
+}
+
+mla_status mla_debug_wg_trace(uint64_t* host, int64_t n, int32_t clear) {
+#ifdef MLA_WG_TRACE
+  if (n < 0 || n > (int64_t)kWgTraceMax * 4 || (n > 0 && !host)) return MLA_ERR_INVALID_ARG;
+  hipError_t e = hipSuccess;
+  if (clear) {
+    static uint64_t zeros[kWgTraceMax * 4];
+    e = hipMemcpyToSymbol(HIP_SYMBOL(mla::g_wg_trace), zeros, sizeof zeros);
+  }
+  if (e == hipSuccess && n > 0) e = hipMemcpyFromSymbol(host, HIP_SYMBOL(mla::g_wg_trace), (size_t)n * 8);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "copying the workgroup timeline");
+#else
+  (void)host;
+  (void)n;
+  (void)clear;
+  snprintf(g_last_error, sizeof g_last_error, "built without MLA_WG_TRACE (see mla_decode_split_amd/build.py)");
+  return MLA_ERR_UNSUPPORTED;
+#endif
 }
 
 }  // extern "C"

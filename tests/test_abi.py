@@ -36,6 +36,14 @@ def test_library_exports_every_declared_function():
     assert all(hasattr(mla, n) for n in _declared_functions() if n != "mla_last_error_string")
 
 
+def test_workgroup_timeline_only_in_the_measurement_build():
+    """The product library carries no timeline: its entry point says so
+    without touching the device."""
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_debug_wg_trace(None, clear=True)
+    assert e.value.status == mla.MLA_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     assert mla.mla_status_string(0) == "MLA_OK"
     assert mla.mla_status_string(2) == "MLA_ERR_UNSUPPORTED"
