@@ -51,9 +51,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # sha256 is 259437c4...351b70.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "code_sha256": "e58f74421166cd111df7d8c3680fe237560444612ab60ac466e65ea5bfb22c80",
-    "fetch_kib": 149906.3,
-    "write_kib": 8225.1,
+    "code_sha256": "7d502d5192579f0e9b1261f7805fd06ad350d712a6c7cd2be6761792641664ec",
+    "fetch_kib": 149906.1,
+    "write_kib": 8224.9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
