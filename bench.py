@@ -51,9 +51,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # sha256 is 259437c4...351b70.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "code_sha256": "7d502d5192579f0e9b1261f7805fd06ad350d712a6c7cd2be6761792641664ec",
-    "fetch_kib": 149906.1,
-    "write_kib": 8224.9,
+    "code_sha256": "020daafa8e2a22bb0813bcd0fd15942f57b5f4a1c6cadf7bc9a37bb6a46f9bba",
+    "fetch_kib": 149907.7,
+    "write_kib": 8224.6,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }

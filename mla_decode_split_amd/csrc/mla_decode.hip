@@ -1415,12 +1415,14 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
   const int64_t d8 = 8 * (wg_hi - r0);
   auto below = [&](int64_t x) -> int { return d8 > x ? (int)std::min<int64_t>((d8 - x + 255) / 256, INT_MAX) : 0; };
   const int f4 = below(4 * (int64_t)wg_rows), f2 = below(2 * (int64_t)wg_rows), f1 = below(wg_rows);
-  int prio = -1;
+  // tile at which the priority changes next (it only falls, at f4, f2 and f1;
+  // the calls come for consecutive tiles from 0)
+  int next_prio = 0;
   auto priority = [&](int i) {
-    const int want = (i < f4) + (i < f2) + (i < f1);
-    if (want != prio) {
-      prio = want;
-      set_priority(prio);
+    if (i == next_prio) {
+      const int want = (i < f4) + (i < f2) + (i < f1);
+      set_priority(want);
+      next_prio = want == 3 ? f4 : want == 2 ? f2 : want == 1 ? f1 : INT_MAX;
     }
   };
   float cs[QW];
