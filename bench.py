@@ -301,6 +301,28 @@ class Timed:
         dev.run_merge(self.plan, self.batch, self.out, self.ws, self.stream)
         return 1e3 * a.elapsed_time(b) / steps
 
+    def ring_read_us(self, steps):
+        """Average duration of mla_debug_stream_ring over this call's KV bytes
+        (the KV copies rotated as for the calls, as many workgroups as stage 1
+        launches): stage 1's memory side with no arithmetic.  fp8 KV only (the
+        ring has the fp8 kernel's geometry); None otherwise."""
+        import torch
+        import mla_decode_split_amd as mla
+
+        if self.w.kv_dtype != "fp8" or self.w.kv_indices is not None or self.kv_bytes % 18432:
+            return None
+        wgs = mla.mla_decode_plan_describe(self.plan)["num_splits"]
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        for i in range(3):
+            mla.mla_debug_stream_ring(self.kvs[i % self.ncopy], self.kv_bytes, wgs, sink, self.stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for i in range(steps):
+            mla.mla_debug_stream_ring(self.kvs[i % self.ncopy], self.kv_bytes, wgs, sink, self.stream)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / steps
+
     def describe(self):
         import mla_decode_split_amd as mla
 
@@ -343,6 +365,7 @@ def main() -> int:
     elapsed = h.time(args.steps, args.warmup)
     # roofline: K stage-1 launches back to back between two events on their stream
     split_us = h.split_launch_us(args.steps)
+    ring_us = h.ring_read_us(args.steps)
     ms_per_step = 1e3 * elapsed / args.steps
     value = h.kv_bytes * args.steps / elapsed / 1e9
     achieved = h.kv_bytes / (split_us * 1e-6) / 1e9
@@ -360,6 +383,10 @@ def main() -> int:
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "read_ceiling_GBs": round(ceiling, 1) if ceiling else None,
         "frac_of_read_ceiling": round(value / ceiling, 4) if ceiling else None,
+        # stage 1's memory side alone (mla_debug_stream_ring over the same bytes)
+        "ring_read_us": round(ring_us, 3) if ring_us else None,
+        "ring_read_GBs": round(h.kv_bytes / (ring_us * 1e-6) / 1e9, 1) if ring_us else None,
+        "stage1_frac_of_ring_read": round(ring_us / split_us, 4) if ring_us else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -404,6 +431,11 @@ def main() -> int:
                    "stage1_us": round(s1, 2), "stage1_frac_of_peak": round(t.kv_bytes / (s1 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "kv_bytes": t.kv_bytes, "kv_copies_rotated": t.ncopy, "num_splits": d["num_splits"],
                    "rows_per_split": d["rows_per_split"], "stage2": d["stage2"]}
+            if q_len == 1:
+                ring = t.ring_read_us(min(steps, 200))
+                if ring:
+                    row["ring_read_us"] = round(ring, 2)
+                    row["stage1_frac_of_ring_read"] = round(ring / s1, 4)
             if not args.no_cpu_baseline and q_len == 1:
                 row["cpu_baseline"] = cpu_baseline(t.w, t.kv_bytes / t.rows, args.cpu_seconds)
             table.append(row)

@@ -334,6 +334,21 @@ mla_status mla_debug_decode(int32_t kv_dtype, const void* codes, const void* sca
 mla_status mla_debug_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /*
+ * Read-bandwidth reference with stage 1's own access pattern (a measurement
+ * aid, defined by none of the pages): `wgs` workgroups, two per CU, each stream
+ * a contiguous share of `bytes` in 18 KB tiles through the four-slot LDS ring
+ * of the fp8 stage-1 kernel (the same 16-byte LDS DMA, waits and two barriers
+ * per tile), with no arithmetic.  Timing it over the bytes of a call gives the
+ * rate the decode's memory side reaches when nothing else runs.
+ *   buf    device, 16-byte aligned; bytes a multiple of 18432, at most about
+ *          4 GB per workgroup share (MLA_ERR_INVALID_ARG otherwise); wgs >= 1.
+ *   sink   device uint32[1]; written only in the (practically impossible) case
+ *          that the XOR of the words it samples equals 0x9E3779B9.
+ * Asynchronous on `stream`.
+ */
+mla_status mla_debug_stream_ring(const void* buf, int64_t bytes, int32_t wgs, uint32_t* sink, void* stream);
+
+/*
  * Per-workgroup timeline of the last stage-1 launch (a measurement aid, defined
  * by none of the pages; for finding where a call's time goes).  Only the
  * library built with -DMLA_WG_TRACE records it (mla_decode_split_amd/build.py,

@@ -91,6 +91,8 @@ def _lib_handle():
         lib.mla_debug_decode.restype = i32
         lib.mla_debug_stream_read.argtypes = [vp, i64, vp, vp]
         lib.mla_debug_stream_read.restype = i32
+        lib.mla_debug_stream_ring.argtypes = [vp, i64, i32, vp, vp]
+        lib.mla_debug_stream_ring.restype = i32
         lib.mla_debug_wg_trace.argtypes = [vp, i64, i32]
         lib.mla_debug_wg_trace.restype = i32
         lib.mla_status_string.argtypes = [i32]
@@ -284,6 +286,12 @@ def mla_debug_stream_read(buf, nbytes: int, sink, stream=None) -> None:
     st = _lib_handle().mla_debug_stream_read(_addr(buf), nbytes, _addr(sink), _stream(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_debug_stream_read")
+
+
+def mla_debug_stream_ring(buf, nbytes: int, wgs: int, sink, stream=None) -> None:
+    st = _lib_handle().mla_debug_stream_ring(_addr(buf), nbytes, wgs, _addr(sink), _stream(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_debug_stream_ring")
 
 
 def mla_debug_wg_trace(host: np.ndarray | None, clear: bool = False) -> None:

@@ -1882,6 +1882,48 @@ __global__ __launch_bounds__(256) void mla_debug_stream_read_kernel(const u32x4*
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = acc.x;
 }
 
+// The read that stage 1's memory side does, with no arithmetic: each workgroup
+// streams its contiguous share of whole 18 KB tiles (fp8 geometry) through the
+// same four-slot LDS ring by the same 16-byte LDS DMA, chunks dealt round robin
+// to the four waves, NS - 2 tiles kept in flight, two workgroup barriers per
+// tile and the refill issued after the second; two workgroups per CU, like the
+// fp8 kernel.  Each tile is touched once in LDS.
+__global__ __launch_bounds__(Geom<DT_FP8>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mla_debug_stream_ring_kernel(const uint8_t* buf, int64_t tiles, uint32_t* sink) {
+  using G = Geom<DT_FP8>;
+  using DM = Dma<DT_FP8, false>;
+  constexpr int NS = RingCfg<DT_FP8, 1>::kStages;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * G::kStageBytes];
+  const int wd = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t t0 = tiles * blockIdx.x / gridDim.x, t1 = tiles * (blockIdx.x + 1) / gridDim.x;
+  const int n = (int)(t1 - t0);
+  if (n <= 0) return;
+  const i32x4 r = make_rsrc(buf + t0 * G::kStageBytes, (uint32_t)((int64_t)n * G::kStageBytes));
+  auto issue = [&](int t) {
+#pragma unroll
+    for (int k = 0; k < DM::kMaxChunksPerWave; ++k) {
+      const int c = wd + DM::kWaves * k;
+      if (c >= G::kRowChunks) break;
+      dma16(r, uniform(lds_addr(ring + (t % NS) * G::kStageBytes + c * 1024)),
+            (uint32_t)(t * G::kRowBytes) + dma_src_offset<DT_FP8>(64 * c + lane));
+    }
+  };
+  const int my_chunks = DM::chunks_of_wave(wd);
+  for (int t = 0; t < NS - 1 && t < n; ++t) issue(t);
+  uint32_t acc = 0;
+  for (int i = 0; i < n; ++i) {
+    if (i + NS - 2 < n)
+      wait_tiles_behind_fixed<DM::kMaxChunksPerWave, NS - 2>(my_chunks);
+    else
+      wait_tiles_behind<DM::kMaxChunksPerWave>(my_chunks, n - 1 - i);
+    lds_barrier();
+    acc ^= *(const uint32_t*)(ring + (i % NS) * G::kStageBytes + 1024 * wd + 16 * lane);
+    lds_barrier();
+    if (i + NS - 1 < n) issue(i + NS - 1);
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace mla
 
 // ==================================================================== host
@@ -2467,6 +2509,18 @@ mla_status mla_debug_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
                      bytes / 16, sink);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the read-ceiling kernel");
+}
+
+mla_status mla_debug_stream_ring(const void* buf, int64_t bytes, int32_t wgs, uint32_t* sink, void* stream) {
+  constexpr int64_t kTileBytes = Geom<DT_FP8>::kStageBytes;
+  if (!buf || !sink || bytes < 0 || bytes % kTileBytes || ((uintptr_t)buf & 15) || wgs < 1 ||
+      bytes / kTileBytes / wgs > (0xFFFFF000ll / kTileBytes))
+    return MLA_ERR_INVALID_ARG;
+  if (bytes == 0) return MLA_OK;
+  hipLaunchKernelGGL(mla_debug_stream_ring_kernel, dim3(wgs), dim3(Geom<DT_FP8>::kThreads), 0, (hipStream_t)stream,
+                     (const uint8_t*)buf, bytes / kTileBytes, sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "launching the ring-read kernel");
 }
 
 mla_status mla_debug_wg_trace(uint64_t* host, int64_t n, int32_t clear) {

@@ -284,6 +284,13 @@ def test_run_argument_errors_before_any_launch():
     assert mla.library().mla_debug_stream_read(A + 8, 32, A, None) == mla.MLA_ERR_INVALID_ARG
     assert mla.library().mla_debug_stream_read(A, 32, None, None) == mla.MLA_ERR_INVALID_ARG
     assert mla.library().mla_debug_stream_read(A, 0, A, None) == mla.MLA_OK                 # nothing to launch
+    ring = mla.library().mla_debug_stream_ring
+    assert ring(A, 18432 + 16, 2, A, None) == mla.MLA_ERR_INVALID_ARG  # not whole 18 KB tiles
+    assert ring(A + 8, 18432, 1, A, None) == mla.MLA_ERR_INVALID_ARG   # misaligned
+    assert ring(A, 18432, 0, A, None) == mla.MLA_ERR_INVALID_ARG       # no workgroups
+    assert ring(A, 18432, 1, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert ring(A, 18432 * (1 << 20), 1, A, None) == mla.MLA_ERR_INVALID_ARG  # a share past 32-bit offsets
+    assert ring(A, 0, 4, A, None) == mla.MLA_OK                             # nothing to launch
 
 
 @pytest.mark.parametrize("kv_dtype,q_len", [("fp8", 1), ("fp8", 2), ("fp8", 4), ("bf16", 1), ("bf16", 2),

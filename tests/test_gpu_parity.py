@@ -617,6 +617,20 @@ def test_first_piece_table_at_its_limit(kv_dtype, groups):
     _compare(_bf16_out_to_f64(o1), ref, f"first-piece table, {groups} workgroups, {kv_dtype}")
 
 
+def test_ring_read_runs_and_leaves_the_sink():
+    """The memory-side reference (stage 1's ring with no arithmetic) streams a
+    buffer in every share shape - more workgroups than tiles, uneven shares -
+    and writes nothing but, with the practically impossible XOR, its sink."""
+    nbytes = 18432 * 1000
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for wgs in (1, 3, 512, 2000):
+        mla.mla_debug_stream_ring(buf, nbytes, wgs, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    assert bool((buf == 1).all())
+
+
 # ------------------------------------------------------------- paired ranges
 
 @pytest.mark.parametrize("skew", [120, 250])
