@@ -51,9 +51,9 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # sha256 is 259437c4...351b70.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "code_sha256": "020daafa8e2a22bb0813bcd0fd15942f57b5f4a1c6cadf7bc9a37bb6a46f9bba",
+    "code_sha256": "099fc2802cd2b275de392f8f5792ff35f2f96d8df6ca0036e652a7baba991c8e",
     "fetch_kib": 149907.7,
-    "write_kib": 8224.6,
+    "write_kib": 8225.7,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
