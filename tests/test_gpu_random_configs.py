@@ -7,7 +7,15 @@ rows, and the planner's inputs (host offsets or not, forced range sizes, the
 CU count, paired ranges with an age skew and XCD grouping).  The output is
 compared element by element with the fp64 oracle, and the workspace starts
 poisoned with NaN.  The draws are a fixed list of seeds, so every case is
-reproducible and printed before it runs."""
+reproducible and printed before it runs.
+
+A second, wider draw mixes in the shapes the first one rarely reaches: several
+hundred short sequences (more than the merge kernel's argument table holds),
+and one long sequence among short ones (a sequence split over many ranges next
+to sequences that share one).  MLA_RANDOM_SEEDS=a:b and MLA_RANDOM_WIDE_SEEDS=a:b
+replace the seed ranges for a longer sweep."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -66,14 +74,43 @@ def _draw(seed):
     return dict(lengths=lengths, q_dtype=q_dtype, kv_dtype=kv_dtype, q_lens=q_lens, cap=cap, page=page, opts=opts)
 
 
-@pytest.mark.parametrize("seed", range(200))
-def test_random_config(seed):
+def _draw_wide(seed):
     c = _draw(seed)
-    what = (f"random #{seed}: bs={len(c['lengths'])} rows={int(c['lengths'].sum())} {c['q_dtype']}/{c['kv_dtype']} "
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xA11]))
+    kind = int(rng.integers(0, 2))
+    if kind == 0:
+        # many short sequences, a fifth of them empty
+        bs = int(rng.integers(500, 900))
+        c["lengths"] = np.where(rng.random(bs) < 0.2, 0, rng.integers(1, 200, bs))
+        rows = int(rng.choice([0, 32, 64]))
+    else:
+        # one long sequence among short ones
+        bs = int(rng.integers(2, 20))
+        c["lengths"] = rng.integers(0, 50, bs)
+        c["lengths"][int(rng.integers(bs))] = int(rng.integers(20000, 60000))
+        rows = int(rng.choice([0, 0, 96, 1024]))
+    if c["q_lens"] is not None:
+        mq = int(c["q_lens"].max())
+        c["q_lens"] = rng.integers(0, mq + 1, bs)
+        c["q_lens"][0] = mq
+    c["opts"] = dict(rows_per_split=rows, use_host_indptr=bool(rng.random() < 0.75))
+    return c
+
+
+def _seeds(var, default):
+    v = os.environ.get(var)
+    if not v:
+        return default
+    a, b = (int(x) for x in v.split(":"))
+    return range(a, b)
+
+
+def _run_case(c, seed, label):
+    what = (f"{label} #{seed}: bs={len(c['lengths'])} rows={int(c['lengths'].sum())} {c['q_dtype']}/{c['kv_dtype']} "
             f"q_lens={'1' if c['q_lens'] is None else 'up to ' + str(int(c['q_lens'].max()))} cap={c['cap']} "
             f"page={c['page']} plan={c['opts']}")
     _say(what)
-    w = synth.make_batch(c["lengths"], c["q_dtype"], c["kv_dtype"], seed=3000 + seed, name=f"random-{seed}",
+    w = synth.make_batch(c["lengths"], c["q_dtype"], c["kv_dtype"], seed=3000 + seed, name=f"{label}-{seed}",
                          q_lens=c["q_lens"])
     w.logit_cap = c["cap"]
     if c["page"]:
@@ -90,3 +127,13 @@ def test_random_config(seed):
     d = mla.mla_decode_plan_describe(plan)
     _say(f"   plan: {d['num_splits']} ranges of {d['rows_per_split']} rows, paired {d['paired_splits']}, "
          f"xcd group {d['xcd_group']}, stage 2 {d['stage2']}, merge batch {d['merge_batch']}")
+
+
+@pytest.mark.parametrize("seed", _seeds("MLA_RANDOM_SEEDS", range(200)))
+def test_random_config(seed):
+    _run_case(_draw(seed), seed, "random")
+
+
+@pytest.mark.parametrize("seed", _seeds("MLA_RANDOM_WIDE_SEEDS", range(1000, 1040)))
+def test_random_config_wide(seed):
+    _run_case(_draw_wide(seed), seed, "wide")
