@@ -15,8 +15,10 @@ Prints one JSON line: value = KV bytes read per second over the timed steps
 calls that follow about 0.1 s of untimed calls which settle the device's
 clocks to this kernel), plus per-call
 microseconds, the stage-1 kernel's roofline (its average launch duration from
-K stage-1 launches back to back between two HIP events on the launch stream)
-and the CPU oracle timed on a bounded sample of the same workload.  The table
+K stage-1 launches back to back between two HIP events on the launch stream),
+stage 1's matrix-unit rate (the method's QK^T and PV flops over the same launch
+time, against the dense bf16 peak) and the CPU oracle timed on a bounded sample
+of the same workload.  The table
 of workloads gives the same figures for each of the five workloads (and the
 headline shape with two and four query rows), each with the oracle timed on a
 bounded sample of that workload.  A plain read kernel over one 1 GiB buffer
@@ -38,6 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 DEFAULT_WORKLOAD = "bs64_kv8192_fp8"
 KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip")
 
@@ -150,6 +153,24 @@ def cpu_baseline(w, kv_bytes_per_row: float, target_s: float) -> dict:
                      f"{dt:.2f} s wall on {threads} threads"}
     res.update(_cpu_description())
     return res
+
+
+def mfma_flop(w) -> int:
+    """The method's matrix work per call: for every (KV row, query row) pair of a
+    sequence, QK^T over 576 dims and PV over 512 columns for 16 heads, 2 flop
+    per multiply-add."""
+    kv = np.diff(np.asarray(w.kv_indptr, dtype=np.int64))
+    q = np.diff(np.asarray(w.qo_indptr, dtype=np.int64))
+    return int(2 * 16 * (576 + 512) * int((kv * q).sum()))
+
+
+def mfma_block(flop: int, us: float) -> dict:
+    """Stage 1's matrix-unit rate from the method's flops and its launch time,
+    against the dense bf16 peak (the PV products are bf16; the rocprofv3
+    MfmaUtil counter per workload is in profiles/)."""
+    achieved = flop / (us * 1e-6) / 1e12
+    return {"flop_per_launch": flop, "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "peak_dtype": "bf16"}
 
 
 def code_sha256(path: str = KERNEL_SRC) -> str:
@@ -397,6 +418,8 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _measured_traffic(h.name), "avg_launch_us": round(split_us, 3),
                      "bytes_per_launch": h.kv_bytes},
+        # the matrix unit is not the bound: stage 1's flop rate against its peak
+        "mfma": mfma_block(mfma_flop(h.w), split_us),
         "plan_us": round(1e6 * h.t_plan, 1),
         "input_generation_s": round(h.t_gen, 2),
     }
@@ -429,6 +452,7 @@ def main() -> int:
                    "GBs": round(t.kv_bytes / (us * 1e-6) / 1e9, 1),
                    "frac_of_peak": round(t.kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "stage1_us": round(s1, 2), "stage1_frac_of_peak": round(t.kv_bytes / (s1 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "stage1_mfma_frac": mfma_block(mfma_flop(t.w), s1)["frac"],
                    "kv_bytes": t.kv_bytes, "kv_copies_rotated": t.ncopy, "num_splits": d["num_splits"],
                    "rows_per_split": d["rows_per_split"], "stage2": d["stage2"]}
             if q_len == 1:

@@ -42,3 +42,15 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_matrix_work_counts_every_kv_row_for_every_query_row():
+    class W:
+        kv_indptr = [0, 3, 3, 8]   # lengths 3, 0, 5
+        qo_indptr = [0, 2, 3, 4]   # query rows 2, 1, 1
+    # (3 * 2 + 0 * 1 + 5 * 1) pairs, each QK^T over 576 dims and PV over 512
+    # columns for 16 heads at 2 flop per multiply-add
+    assert bench.mfma_flop(W) == 11 * 2 * 16 * (576 + 512)
+    b = bench.mfma_block(bench.mfma_flop(W), 1.0)
+    assert b["unit"] == "TFLOP/s" and b["peak"] == 2500.0
+    assert abs(b["frac"] - round(11 * 34816 / 1e-6 / 1e12 / 2500.0, 4)) < 1e-12
