@@ -428,9 +428,11 @@ struct Elem16<lds_cbytes> {
 // would otherwise treat every later LDS read as dependent on this write and
 // wait for all DMA in flight, which serialises the tile ring.  Completion is
 // tracked explicitly with s_waitcnt vmcnt before a tile is read.  m0 is not
-// used for anything else in these kernels.
+// used for anything else in these kernels.  The loads are non-temporal (nt):
+// every KV byte is read once, and with the streaming cache policy the same
+// ring moves 302 MB in 44 us instead of 50 (6.9 against 6.0 TB/s).
 __device__ inline void dma16(i32x4 r, uint32_t lds_base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds_base), "v"(voff), "s"(r)
                : "memory", "m0");
 }
 
@@ -438,7 +440,7 @@ __device__ inline void dma16(i32x4 r, uint32_t lds_base, uint32_t voff) {
 // before anything else (no LDS access precedes the wait that consumes them),
 // so that the scalar loads the compiler places after them stay scalar.
 __device__ inline void dma16_first(i32x4 r, uint32_t lds_base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r) : "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds_base), "v"(voff), "s"(r) : "m0");
 }
 
 // 4 bytes per active lane from rsrc + voff into LDS at lds_base + 4 * lane (the
@@ -1792,14 +1794,15 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MergeParams p, Tab tab) 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
   for (int32_t base = g0; base <= g1; base += NB) {
     // straight-line loads (slots past g1 re-read slot g1 and get weight 0), so
-    // that they are all in flight before the first is used
+    // that they are all in flight before the first is used; the partials are
+    // read once, non-temporal (0.2-1 us faster per call than cached loads)
     float lse[NB];
     u32x4 u[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int64_t slot = (int64_t)merge_slot(p.cut, std::min(base + k, g1), g0) * QL + tq;
       lse[k] = p.part_lse[slot * kHeads + h];
-      u[k] = *(const u32x4*)(p.part_o + (slot * kHeads + h) * kV + 8 * t);
+      u[k] = __builtin_nontemporal_load((const u32x4*)(p.part_o + (slot * kHeads + h) * kV + 8 * t));
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k)
@@ -1865,20 +1868,24 @@ __global__ void mla_debug_decode_kernel(int kv_dtype, const uint8_t* codes, cons
 
 // ---------------------------------------------------------------- read ceiling
 
-// Streams a buffer with 16-byte non-temporal loads, four in flight per thread,
-// and folds what it reads into one word that is stored only if it equals a
-// value no sane input produces (so the loads cannot be removed).
+// Streams a buffer with 16-byte non-temporal loads: each workgroup reads its
+// own contiguous share, 4 KB per load instruction of its 256 threads and four
+// in flight (measured 6.8-7.1 TB/s over 1 GiB, against 5.9 TB/s for a grid
+// stride, where consecutive workgroups read adjacent 4 KB blocks).  It folds
+// what it reads into one word that is stored only if it equals a value no
+// sane input produces (so the loads cannot be removed).
 __global__ __launch_bounds__(256) void mla_debug_stream_read_kernel(const u32x4* __restrict__ p, int64_t n16,
                                                                     uint32_t* sink) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t share = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * share, hi = std::min<int64_t>(lo + share, n16);
   u32x4 acc = {0, 0, 0, 0};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride), d = __builtin_nontemporal_load(p + i + 3 * stride);
+  int64_t i = lo + threadIdx.x;
+  for (; i + 3 * 256 < hi; i += 4 * 256) {
+    const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + 256);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 512), d = __builtin_nontemporal_load(p + i + 768);
     acc ^= a ^ b ^ c ^ d;
   }
-  for (; i < n16; i += stride) acc ^= p[i];
+  for (; i < hi; i += 256) acc ^= p[i];
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = acc.x;
 }
 
