@@ -1998,8 +1998,10 @@ RingInfo ring_info_for(int kv_dtype, int ql, bool paged) {
 }
 
 // Per mille of R moved to the first workgroup on each CU when there are more
-// workgroups than CUs (see Cut).
-constexpr int kDefaultAgeSkew = 150;
+// workgroups than CUs (see Cut).  Swept with the non-temporal KV loads: 120
+// against 80 / 100 / 150 ran bs 256 in 183.9 against 187.5 / 184.6 / 188.0 us
+// per call, bs 64 within 0.3 us.
+constexpr int kDefaultAgeSkew = 120;
 
 // Smallest row range worth a workgroup: below it the partial write-back and the
 // merge cost more than the extra parallelism gains.
