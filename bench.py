@@ -51,12 +51,12 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # its comments removed and its whitespace collapsed (code_sha256 below), so
 # that editing a comment keeps them and changing code drops them (traffic is
 # then reported as null).  The counters were taken on the source whose full
-# sha256 is a9f980f7...b540bcf.
+# sha256 is 0a2f982b...dccb547e.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "code_sha256": "c4b65d0ae5cb357def77aa3cfa043f1b0713591fd45f6e8f13c93eb237ed5049",
-    "fetch_kib": 149910.8,
-    "write_kib": 8224.5,
+    "code_sha256": "763122fdfa9f672f37eac8e610548c15ea8563063fba5069d5afcbc438b9adec",
+    "fetch_kib": 149911.3,
+    "write_kib": 8224.2,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
