@@ -436,6 +436,15 @@ __device__ inline void dma16(i32x4 r, uint32_t lds_base, uint32_t voff) {
                : "memory", "m0");
 }
 
+// The same DMA with the default cache policy, for E2M1 rows and scale windows
+// gathered one by one (pages of one row: 288-byte rows and 32-byte windows at
+// scattered places, where the non-temporal policy measured 8 us slower on the
+// ragged MXFP4 batch; with pages of 16 rows it is 4 us faster).
+__device__ inline void dma16_cached(i32x4 r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
 // The same DMA without a memory clobber, for the loads a workgroup issues
 // before anything else (no LDS access precedes the wait that consumes them),
 // so that the scalar loads the compiler places after them stay scalar.
@@ -1231,7 +1240,8 @@ __device__ inline void set_priority(int prio) {
 // One piece: rows [r0, r0 + n) of a sequence whose query rows are qrow0 ..
 // qrow0 + nq - 1 (nq in [1, QL]; the operands of tokens past nq repeat the
 // last row and their results are dropped).
-template <int QF, int KF, int QL, bool CAP, bool PAGED>
+// G1: E2M1 KV in pages of one row (its gathers take the default cache policy).
+template <int QF, int KF, int QL, bool CAP, bool PAGED, bool G1 = false>
 __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, uint8_t* pbuf, int32_t* idxring,
                             uint8_t* dtab,
                             int64_t qrow0, int nq, int64_t r0,
@@ -1294,12 +1304,20 @@ __device__ void split_piece(const SplitParams& p, uint8_t* ring, float* xchg, ui
       if (PAGED && c < G::kRowChunks) {
         // physical row of this lane's tile row (an index outside the buffer
         // wraps or lands past its end, where the read returns zero)
-        dma16(rk, uniform(lds_addr(stage + c * 1024)), (uint32_t)ix[prow[k]] * (uint32_t)G::kRow + src[k]);
+        const uint32_t off = (uint32_t)ix[prow[k]] * (uint32_t)G::kRow + src[k];
+        if constexpr (G1)
+          dma16_cached(rk, uniform(lds_addr(stage + c * 1024)), off);
+        else
+          dma16(rk, uniform(lds_addr(stage + c * 1024)), off);
       } else if (PAGED) {
         // E8M0 bytes of tile row lane >> 1: the aligned 32-byte window holding
         // its 18 (two 16-byte halves), and the row's offset in it
         const uint32_t sb = (uint32_t)ix[lane >> 1] * (uint32_t)kScaleRow;
-        dma16(rs, uniform(lds_addr(stage + G::kRowBytes)), (sb & ~15u) + 16u * (uint32_t)(lane & 1));
+        const uint32_t soff = (sb & ~15u) + 16u * (uint32_t)(lane & 1);
+        if constexpr (G1)
+          dma16_cached(rs, uniform(lds_addr(stage + G::kRowBytes)), soff);
+        else
+          dma16(rs, uniform(lds_addr(stage + G::kRowBytes)), soff);
         if ((lane & 1) == 0) dtab[(t % NS) * kTile + (lane >> 1)] = (uint8_t)(sb & 15u);
       } else if (c < G::kRowChunks) {
         dma16(rk, uniform(lds_addr(stage + c * 1024)), (uint32_t)(t * G::kRowBytes) + src[k]);
@@ -1537,7 +1555,7 @@ struct NoSplitTable {
 };
 static_assert(sizeof(SplitParams) + sizeof(SplitTable) <= 4096, "kernel arguments within 4 KB");
 
-template <int QF, int KF, int QL, bool CAP, bool PAGED, typename Tab>
+template <int QF, int KF, int QL, bool CAP, bool PAGED, typename Tab, bool G1>
 __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attribute__((amdgpu_waves_per_eu(
     Ring<KF, QL, PAGED>::kWgsPerCu * RowSplit<QL>::kGroups,
     Ring<KF, QL, PAGED>::kWgsPerCu * RowSplit<QL>::kGroups))) void mla_split_kernel(SplitParams p, Tab tab) {
@@ -1594,7 +1612,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
         const bool ok = pb >= 0 && pe >= pb;
         ps = PageSpan{ok ? pb : 0, ok ? pe - pb : 0, (int32_t)(lo - s)};
       }
-      split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab,
+      split_piece<QF, KF, QL, CAP, PAGED, G1>(p, ring, xchg, pbuf, idxring, dtab,
                                           b0, 1, lo, n_first,
                                           piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, (int32_t)(hi - lo),
                                           ps, false);
@@ -1636,7 +1654,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       for (int t = 1; t < NS - 1; ++t) issue(t);
       const int64_t s0 = (v >> 30) & 1u ? lo : lo - 1;  // only "before lo" matters below lo
       const int64_t e0 = (v >> 31) ? lo + n_first : hi + 1;
-      split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab,
+      split_piece<QF, KF, QL, CAP, PAGED, G1>(p, ring, xchg, pbuf, idxring, dtab,
                                           b0, 1, lo, n_first,
                                           piece_slot(s0, e0, lo, hi, gi), score_scale, out_scale, hi, (int32_t)(hi - lo),
                                           PageSpan{lo, p.total_kv - lo, 0}, true);
@@ -1696,7 +1714,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       const bool ok = pb >= 0 && pe >= pb;
       ps = PageSpan{ok ? pb : 0, ok ? pe - pb : 0, (int32_t)(r0 - s)};
     }
-    split_piece<QF, KF, QL, CAP, PAGED>(p, ring, xchg, pbuf, idxring, dtab, qrow0, nq,
+    split_piece<QF, KF, QL, CAP, PAGED, G1>(p, ring, xchg, pbuf, idxring, dtab, qrow0, nq,
                             r0, (int)(r1 - r0), slot, score_scale, out_scale, hi, (int32_t)(hi - lo), ps, false);
     lds_barrier();  // the next piece refills the ring
   }
@@ -2015,30 +2033,41 @@ int min_rows_for(int kv_dtype) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-template <int QF, int KF, bool CAP, bool PAGED>
+template <int QF, int KF, bool CAP, bool PAGED, bool G1>
 void launch_split_v(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
   const dim3 grid(pl->num_wgs), block(Geom<KF>::kThreads * (pl->ql == 4 ? RowSplit<4>::kGroups : 1));
   {
     if (pl->ql == 1 && pl->has_split_table) {
-      hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, SplitTable>), grid, block, 0, st, sp,
+      hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, SplitTable, G1>), grid, block, 0, st, sp,
                          pl->split_table);
       return;
     }
   }
   if (pl->ql == 1)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, NoSplitTable>), grid, block, 0, st, sp, NoSplitTable{});
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 1, CAP, PAGED, NoSplitTable, G1>), grid, block, 0, st, sp, NoSplitTable{});
   else if (pl->ql == 2)
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2, CAP, PAGED, NoSplitTable>), grid, block, 0, st, sp, NoSplitTable{});
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 2, CAP, PAGED, NoSplitTable, G1>), grid, block, 0, st, sp, NoSplitTable{});
   else
-    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4, CAP, PAGED, NoSplitTable>), grid, block, 0, st, sp, NoSplitTable{});
+    hipLaunchKernelGGL((mla_split_kernel<QF, KF, 4, CAP, PAGED, NoSplitTable, G1>), grid, block, 0, st, sp, NoSplitTable{});
+}
+
+template <int QF, int KF, bool PAGED, bool G1>
+void launch_split_c(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
+  if (pl->prob.logit_cap > 0.f)
+    launch_split_v<QF, KF, true, PAGED, G1>(pl, sp, st);
+  else
+    launch_split_v<QF, KF, false, PAGED, G1>(pl, sp, st);
 }
 
 template <int QF, int KF, bool PAGED>
 void launch_split_p(const mla_plan* pl, const SplitParams& sp, hipStream_t st) {
-  if (pl->prob.logit_cap > 0.f)
-    launch_split_v<QF, KF, true, PAGED>(pl, sp, st);
-  else
-    launch_split_v<QF, KF, false, PAGED>(pl, sp, st);
+  if constexpr (PAGED && KF == DT_MXFP4) {
+    if (pl->prob.kv_paged == 1) {
+      launch_split_c<QF, KF, PAGED, true>(pl, sp, st);
+      return;
+    }
+  }
+  launch_split_c<QF, KF, PAGED, false>(pl, sp, st);
 }
 
 template <int QF, int KF>
