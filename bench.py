@@ -51,12 +51,12 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # its comments removed and its whitespace collapsed (code_sha256 below), so
 # that editing a comment keeps them and changing code drops them (traffic is
 # then reported as null).  The counters were taken on the source whose full
-# sha256 is 0a2f982b...dccb547e.
+# sha256 is 5b295dc6...aea260f9.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "code_sha256": "763122fdfa9f672f37eac8e610548c15ea8563063fba5069d5afcbc438b9adec",
-    "fetch_kib": 149911.3,
-    "write_kib": 8224.2,
+    "code_sha256": "340ab14bdb4643cc56a86277955db7c9cd3e3efee46b5d42cbe83f5e0b62c152",
+    "fetch_kib": 149909.1,
+    "write_kib": 8224.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
