@@ -323,9 +323,10 @@ mla_status mla_debug_decode(int32_t kv_dtype, const void* codes, const void* sca
 /*
  * Read-bandwidth reference for reports (not part of the decode, and defined by
  * none of the pages; a measurement aid): one launch
- * that reads `bytes` of device memory at `buf` with plain 16-byte loads and
- * nothing else, so that timing it gives the HBM read rate this device
- * sustains, against which the decode's rate can be set.
+ * that reads `bytes` of device memory at `buf` with 16-byte non-temporal loads
+ * (4096 workgroups, each streaming its own contiguous share) and nothing else,
+ * so that timing it gives the HBM read rate this device sustains, against
+ * which the decode's rate can be set.
  *   buf    device, 16-byte aligned; bytes a multiple of 16 (MLA_ERR_INVALID_ARG otherwise).
  *   sink   device uint32[1]; written only in the (practically impossible) case that
  *          the XOR of everything read equals 0x9E3779B9.
