@@ -451,6 +451,12 @@ __device__ inline void dma16_cached(i32x4 r, uint32_t lds_base, uint32_t voff) {
 __device__ inline void dma16_first(i32x4 r, uint32_t lds_base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds_base), "v"(voff), "s"(r) : "m0");
 }
+// The same with the default cache policy, for the query row: every workgroup
+// of a sequence reads it, and the later ones find it in L2 (bs 32 stage 1
+// 11.1 -> 10.3 us against the non-temporal form).
+__device__ inline void dma16_first_cached(i32x4 r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r) : "m0");
+}
 
 // 4 bytes per active lane from rsrc + voff into LDS at lds_base + 4 * lane (the
 // paged-KV index staging; tracked with vmcnt like dma16).
@@ -1650,7 +1656,7 @@ __global__ __launch_bounds__(Geom<KF>::kThreads * RowSplit<QL>::kGroups) __attri
       constexpr uint32_t kQBytes = kHeads * kQK * (QF == DT_BF16 ? 2 : 1);
       const i32x4 rq = make_rsrc(p.q + (int64_t)b0 * kQBytes, kQBytes);
       for (int c = wd; c < (int)(kQBytes / 1024); c += DM::kWaves)
-        dma16_first(rq, uniform(lds_addr(ring + (NS - 1) * RG::kStageBytes + c * 1024)), (uint32_t)(c * 1024 + 16 * lane));
+        dma16_first_cached(rq, uniform(lds_addr(ring + (NS - 1) * RG::kStageBytes + c * 1024)), (uint32_t)(c * 1024 + 16 * lane));
       for (int t = 1; t < NS - 1; ++t) issue(t);
       const int64_t s0 = (v >> 30) & 1u ? lo : lo - 1;  // only "before lo" matters below lo
       const int64_t e0 = (v >> 31) ? lo + n_first : hi + 1;
