@@ -51,11 +51,11 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decode_split_amd", "csrc", "mla_decode.hip"
 # its comments removed and its whitespace collapsed (code_sha256 below), so
 # that editing a comment keeps them and changing code drops them (traffic is
 # then reported as null).  The counters were taken on the source whose full
-# sha256 is 5b295dc6...aea260f9.
+# sha256 is 94e7d37e...c16d6a8d.
 TRAFFIC_MEASURED = {
     "workload": DEFAULT_WORKLOAD,
-    "code_sha256": "340ab14bdb4643cc56a86277955db7c9cd3e3efee46b5d42cbe83f5e0b62c152",
-    "fetch_kib": 149909.1,
+    "code_sha256": "0090a0d63fc373d41d71d6fc4d7fa5f8630579376d244f2711498ce12743093a",
+    "fetch_kib": 149906.6,
     "write_kib": 8224.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
